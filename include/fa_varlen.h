@@ -1,0 +1,146 @@
+/*
+ * fa_varlen.h -- C ABI of the MI355X (gfx950) varlen flash-attention forward.
+ *
+ * One operation: the forward pass of softmax attention over sequences packed
+ * back to back ("varlen"), with grouped-query heads, a softmax scale, a
+ * left/right key window around the bottom-right aligned diagonal, and an
+ * optional paged K/V cache read through a per-sequence block table.
+ *
+ * The operation and its argument contract are those of candle's
+ * FlashAttentionVarLen forward (huggingface/candle, candle-flash-attn), as the
+ * error-explainer pages for it describe:
+ *   - page "flash-attn-varlen expects input tensors of rank 3", sections
+ *     What it means and Source: q is rank 3 (total_q, num_heads, head_dim);
+ *     without a block table k and v are rank 3 too;
+ *   - page "flash-attn-varlen paged expects k/v tensors of rank 4", sections
+ *     What it means and Source: with a block table, k and v are rank-4 pools
+ *     (num_blocks, page_block_size, num_heads_k, head_dim); the last dim of
+ *     q, k and v must be contiguous;
+ *   - page "paged flash-attn requires page_block_size", section Source: v must
+ *     have k's shape, k's head size must be q's, a page size must be given;
+ *   - page "page_block_size ... does not match k shape", section What it
+ *     means: the page size argument must equal k's dim 1;
+ *   - page "paged flash-attn requires page_block_size to be a multiple of 32",
+ *     section Source: the page size must be a multiple of 32, the head size at
+ *     most 512, and without paging k/v must be (total_k, num_heads_k, head_dim).
+ * The checks run in that order and the error texts are kept identical to the
+ * quoted ones, because callers match on them.
+ *
+ * Ownership: the caller owns every buffer (inputs, out, softmax_lse,
+ * workspace) and the stream.  The library allocates and frees nothing, keeps
+ * no state between calls other than the thread-local error text, and never
+ * synchronizes the device: fa_varlen_fwd only enqueues kernels on `stream`.
+ *
+ * Errors: every function returns FA_OK (0) or one of the FA_ERR_* codes; the
+ * text of the last error on the calling thread is returned by fa_last_error().
+ * On an error nothing is launched and no output is touched.  Faults inside the
+ * kernels (for instance a block id outside the pool) surface at the caller's
+ * next synchronization, as with any asynchronous device work.
+ */
+#ifndef FA_VARLEN_H
+#define FA_VARLEN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+enum fa_dtype { FA_DTYPE_BF16 = 1, FA_DTYPE_I32 = 2 };
+
+/* status codes */
+enum fa_status {
+    FA_OK = 0,
+    FA_ERR_RANK = 1,         /* q/k/v/out/block_table rank */
+    FA_ERR_CONTIGUOUS = 2,   /* last dim not contiguous */
+    FA_ERR_SHAPE = 3,        /* shapes disagree */
+    FA_ERR_PAGE_SIZE = 4,    /* page_block_size missing, mismatched or not a multiple of 32 */
+    FA_ERR_HEAD_DIM = 5,     /* head_dim > 512 or < 1 */
+    FA_ERR_DTYPE = 6,        /* not bf16 (tensors) / int32 (block_table) */
+    FA_ERR_ARGUMENT = 7,     /* null pointer, negative batch, heads not divisible, size limits */
+    FA_ERR_WORKSPACE = 8,    /* workspace missing or smaller than fa_varlen_workspace_bytes() */
+    FA_ERR_DEVICE = 9,       /* a pointer is not device memory */
+    FA_ERR_HIP = 10          /* the HIP runtime refused a launch */
+};
+
+/*
+ * A strided view.  `data` is the address of element (0, ..., 0) with any view
+ * offset already applied (candle's start_offset); strides are in elements.
+ * Only shape[0..rank) and stride[0..rank) are read.
+ */
+typedef struct fa_tensor {
+    void*   data;
+    int32_t dtype;     /* enum fa_dtype */
+    int32_t rank;      /* 0..4 */
+    int64_t shape[4];
+    int64_t stride[4];
+} fa_tensor;
+
+/*
+ * fa_varlen_check -- the shape/stride/dtype contract alone.  Pure host code:
+ * no pointer is dereferenced and no HIP call is made, so it runs without a GPU.
+ *
+ *   q            (total_q, num_heads, head_dim) bf16, last dim contiguous
+ *   k, v         paged: (num_blocks, page_block_size, num_heads_k, head_dim)
+ *                non-paged: (total_k, num_heads_k, head_dim); bf16, last dim contiguous
+ *   out          same shape as q, bf16, last dim contiguous (may be NULL here)
+ *   batch        number of sequences (>= 0)
+ *   block_table  NULL = non-paged; else int32 (batch, max_blocks_per_seq), last dim contiguous
+ *   page_block_size  0 = not given; must equal k.shape[1] and be a multiple of 32 when paged;
+ *                ignored without a block table
+ * Returns FA_OK or the first failing check's code (text in fa_last_error()).
+ */
+int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                    const fa_tensor* out, int32_t batch, const fa_tensor* block_table,
+                    int32_t page_block_size);
+
+/*
+ * fa_varlen_workspace_bytes -- device scratch that fa_varlen_fwd needs for the
+ * same arguments (split-KV partial outputs).  Runs fa_varlen_check first.
+ * Depends on shapes only (never on sequence lengths, which live on the device).
+ * Writes 0 when the call needs no workspace.
+ */
+int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                              int32_t batch, const fa_tensor* block_table,
+                              int32_t page_block_size, size_t* bytes);
+
+/*
+ * fa_varlen_fwd -- enqueue the forward pass on `stream` (a hipStream_t; NULL =
+ * the null stream).
+ *
+ *   cu_seqlens_q, cu_seqlens_k  device int32 arrays of batch+1 cumulative lengths,
+ *       starting at 0.  Sequence b owns query rows [cu_q[b], cu_q[b+1]) of q/out
+ *       and Lk_b = cu_k[b+1] - cu_k[b] keys: non-paged, rows [cu_k[b], cu_k[b+1])
+ *       of k/v; paged, logical key j lives in pool block block_table[b][j / P],
+ *       slot j % P (P = page_block_size).  Rows of out past cu_q[batch] are not
+ *       written.  Contents are not validated (monotone offsets, block ids inside
+ *       the pool, Lk_b <= max_blocks_per_seq * P are the caller's promise).
+ *   softmax_scale  multiplies q.k before the softmax.
+ *   window_left, window_right  query row i of a sequence sits at key position
+ *       a = i + Lk - Lq; key j is visible iff j >= a - window_left (when
+ *       window_left >= 0) and j <= a + window_right (when window_right >= 0).
+ *       Negative = unbounded; causal is (-1, 0).  Query head h reads key/value
+ *       head h / (num_heads / num_heads_k).  A row that sees no key gets out = 0.
+ *   softmax_lse  NULL, or device fp32 [num_heads][total_q]: natural-log
+ *       sum of exp of the scaled scores per row (-inf for a row that sees no key).
+ *   workspace, workspace_bytes  device scratch of at least
+ *       fa_varlen_workspace_bytes(); may be NULL when that is 0.
+ * The call is asynchronous; out must not alias q, k or v.
+ */
+int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                  const fa_tensor* out, const int32_t* cu_seqlens_q,
+                  const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
+                  int32_t page_block_size, float softmax_scale, int32_t window_left,
+                  int32_t window_right, float* softmax_lse, void* workspace,
+                  size_t workspace_bytes, void* stream);
+
+/* Text of the last non-zero status returned on this thread ("" if none). */
+const char* fa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_VARLEN_H */

@@ -1,0 +1,235 @@
+"""C-ABI library: symbols, the argument contract and its error texts (CPU only).
+
+The contract and its order come from candle's FlashAttentionVarLen forward as
+the error-explainer pages quote it; the expected texts are read from
+tests/golden/error_messages.txt (each line cites its page).  No compute call is
+made here: fa_varlen_check and fa_varlen_workspace_bytes are pure host code.
+"""
+import os
+import re
+
+import pytest
+
+import varlen_flash_attention_fa_amd as fa
+from varlen_flash_attention_fa_amd import desc, FA_DTYPE_BF16, FA_DTYPE_I32
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.lib_path()):
+        from varlen_flash_attention_fa_amd import build
+        build.build()
+    return fa.load()
+
+
+def golden():
+    rows = []
+    for line in open(os.path.join(ROOT, "tests", "golden", "error_messages.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        code, text, cite = [x.strip() for x in line.split("|")]
+        rows.append((int(code), text, cite))
+    return rows
+
+
+def render(template, **vals):
+    """Fill a golden template: {name} / {name:?} from vals, bare {:?} in order."""
+    seq = list(vals.pop("_seq", []))
+    out = template
+    for key, val in vals.items():
+        out = out.replace("{%s:?}" % key, val).replace("{%s}" % key, val)
+    while "{:?}" in out:
+        out = out.replace("{:?}", seq.pop(0), 1)
+    return out
+
+
+def tmpl(prefix):
+    hits = [g for g in golden() if g[1] == prefix] or [g for g in golden() if g[1].startswith(prefix)]
+    assert len(hits) == 1, prefix
+    return hits[0]
+
+
+def check(q, k, v, out=None, batch=2, bt=None, page=0):
+    rc = fa.fa_varlen_check(q, k, v, out, batch, bt, page)
+    return rc, fa.fa_last_error() if rc else ""
+
+
+def dl(xs):
+    return "[" + ", ".join(str(x) for x in xs) + "]"
+
+
+# ------------------------------------------------------------------ symbols
+
+def test_exports_every_declared_symbol(lib):
+    header = open(os.path.join(ROOT, "include", "fa_varlen.h")).read()
+    names = re.findall(r"^(?:int|size_t|const char\*)\s+(fa_\w+)\s*\(", header, re.M)
+    assert {"fa_varlen_check", "fa_varlen_workspace_bytes", "fa_varlen_fwd",
+            "fa_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_every_golden_text_is_in_the_library_source():
+    src = open(os.path.join(ROOT, "varlen_flash_attention_fa_amd", "csrc", "fa_api.cpp")).read()
+    for code, text, _ in golden():
+        fixed = re.split(r"\{[^}]*\}", text)[0].strip()
+        assert fixed in src, text
+
+
+# --------------------------------------------------------------- valid calls
+
+Q = desc([86, 4, 64])
+K3 = desc([86, 2, 64])
+BT = desc([3, 4], dtype=FA_DTYPE_I32)
+KP = desc([10, 32, 2, 64])
+
+
+def test_valid_nonpaged_and_paged(lib):
+    assert check(Q, K3, K3, Q, batch=3)[0] == 0
+    assert check(Q, KP, KP, Q, batch=3, bt=BT, page=32)[0] == 0
+
+
+def test_page_size_without_block_table_is_ignored(lib):
+    # page_block_size only matters once a block table makes the call paged
+    assert check(Q, K3, K3, Q, batch=3, page=16)[0] == 0
+
+
+# -------------------------------------------------------- quoted checks, order
+
+def test_rank3_message(lib):
+    code, t, _ = tmpl("flash-attn-varlen expects input tensors of rank 3")
+    rc, msg = check(desc([2, 86, 4, 64]), K3, K3)
+    assert rc == code and msg == render(t, q_rank="4", k_rank="3", v_rank="3")
+    rc, msg = check(Q, desc([86, 2, 64]), desc([1, 86, 2, 64]))
+    assert rc == code and msg == render(t, q_rank="3", k_rank="3", v_rank="4")
+    assert not msg.endswith(")")   # the quoted text has no closing parenthesis
+
+
+def test_rank4_message_when_paged(lib):
+    code, t, _ = tmpl("flash-attn-varlen paged expects")
+    rc, msg = check(Q, K3, K3, batch=3, bt=BT, page=32)
+    assert rc == code and msg == render(t, k_rank="3", v_rank="3")
+    # q of the wrong rank is reported by the rank-3 check first, even when paged
+    rc, msg = check(desc([86, 4]), K3, K3, batch=3, bt=BT, page=32)
+    assert msg.startswith("flash-attn-varlen expects input tensors of rank 3")
+
+
+def test_contiguity_messages_in_order(lib):
+    qs = desc([86, 4, 64], [512, 128, 2])
+    ks = desc([86, 2, 64], [256, 128, 2])
+    for name, args, stride in (("q", (qs, ks, ks), [512, 128, 2]), ("k", (Q, ks, ks), [256, 128, 2]),
+                               ("v", (Q, K3, ks), [256, 128, 2])):
+        code, t, _ = tmpl("the last dim of %s" % name)
+        rc, msg = check(*args, batch=3)
+        assert rc == code and msg == render(t, **{"%s_stride" % name: dl(stride)})
+
+
+def test_paged_shape_chain_order(lib):
+    # v differs from k -> reported before anything about q or page size
+    code, t, _ = tmpl("shape mismatch k")
+    v_bad = desc([10, 32, 2, 32])
+    rc, msg = check(Q, KP, v_bad, batch=3, bt=BT, page=0)
+    assert rc == code and msg == render(t, _seq=[dl([10, 32, 2, 64]), dl([10, 32, 2, 32])])
+    # head size of k differs from q -> before the page size checks
+    code, t, _ = tmpl("shape mismatch q {:?} and k")
+    k_bad = desc([10, 32, 2, 80])
+    rc, msg = check(Q, k_bad, k_bad, batch=3, bt=BT, page=0)
+    assert rc == code and msg == render(t, _seq=[dl([86, 4, 64]), dl([10, 32, 2, 80])])
+
+
+def test_missing_page_size(lib):
+    code, t, _ = tmpl("paged flash-attn requires page_block_size")
+    for page in (0, -32):
+        rc, msg = check(Q, KP, KP, batch=3, bt=BT, page=page)
+        assert rc == code and msg == t
+
+
+def test_page_size_mismatch(lib):
+    code, t, _ = tmpl("page_block_size {")
+    rc, msg = check(Q, KP, KP, batch=3, bt=BT, page=64)
+    assert rc == code and msg == render(t, page_block_size_arg="64", _seq=[dl([10, 32, 2, 64])])
+    assert "does not match k shape" in msg
+
+
+def test_page_size_multiple_of_32(lib):
+    code, t, _ = tmpl("paged flash-attn requires page_block_size to be")
+    for p in (16, 48, 33):
+        k = desc([10, p, 2, 64])
+        rc, msg = check(Q, k, k, batch=3, bt=BT, page=p)
+        assert rc == code and msg == render(t, page_block_size=str(p))
+        assert "multiple of 32" in msg
+    for p in (32, 64, 96, 128, 256):
+        k = desc([10, p, 2, 64])
+        assert check(Q, k, k, batch=3, bt=BT, page=p)[0] == 0
+
+
+def test_paged_head_size_limit(lib):
+    code, t, _ = tmpl("paged flash-attn supports head sizes")
+    q = desc([5, 2, 520])
+    k = desc([4, 32, 1, 520])
+    rc, msg = check(q, k, k, batch=3, bt=BT, page=32)
+    assert rc == code and msg == render(t, head_size_og="520")
+    q = desc([5, 2, 512])
+    k = desc([4, 32, 1, 512])
+    assert check(q, k, k, batch=3, bt=BT, page=32)[0] == 0
+
+
+def test_nonpaged_kv_shape(lib):
+    code, t, _ = tmpl("shape mismatch q {:?} and k")
+    k_bad = desc([86, 2, 32])
+    rc, msg = check(Q, k_bad, K3, batch=3)
+    assert rc == code and msg == render(t, _seq=[dl([86, 4, 64]), dl([86, 2, 32])])
+    code, t, _ = tmpl("shape mismatch q {:?} and v")
+    for v_bad in (desc([85, 2, 64]), desc([86, 1, 64]), desc([86, 2, 63])):
+        rc, msg = check(Q, K3, v_bad, batch=3)
+        assert rc == code and msg == render(t, _seq=[dl([86, 4, 64]), dl(list(v_bad.shape)[:3])])
+
+
+def test_block_table_checks(lib):
+    code, t, _ = tmpl("block_table last dimension")
+    bt = desc([3, 4], [8, 2], dtype=FA_DTYPE_I32)
+    rc, msg = check(Q, KP, KP, batch=3, bt=bt, page=32)
+    assert rc == code and msg == t
+    rc, msg = check(Q, KP, KP, batch=2, bt=BT, page=32)
+    assert rc == 3 and "block_table" in msg
+    rc, msg = check(Q, KP, KP, batch=3, bt=desc([3, 4], dtype=FA_DTYPE_BF16), page=32)
+    assert rc == 6
+
+
+# ------------------------------------------------------------ added checks
+
+def test_dtype_heads_and_out(lib):
+    assert check(desc([86, 4, 64], dtype=FA_DTYPE_I32), K3, K3)[0] == 6
+    rc, msg = check(desc([86, 3, 64]), K3, K3, batch=3)
+    assert rc == 7 and "multiple" in msg
+    rc, msg = check(Q, K3, K3, out=desc([86, 4, 32]), batch=3)
+    assert rc == 3 and "out" in msg
+    rc, msg = check(Q, K3, K3, out=desc([86, 4, 64], [256, 64, 2]), batch=3)
+    assert rc == 2 and "out" in msg
+    rc, msg = check(desc([5, 2, 600]), desc([5, 1, 600]), desc([5, 1, 600]), batch=1)
+    assert rc == 5
+    assert check(Q, K3, K3, batch=-1)[0] == 7
+
+
+def test_first_failing_check_wins(lib):
+    # several problems at once: rank beats contiguity beats shapes beats page size
+    q4 = desc([2, 43, 4, 64], [1, 1, 1, 2])
+    assert check(q4, K3, K3)[1].startswith("flash-attn-varlen expects input tensors of rank 3")
+    ks = desc([10, 16, 2, 64], [2048, 128, 64, 2])
+    msg = check(Q, ks, ks, batch=3, bt=BT, page=0)[1]
+    assert msg.startswith("the last dim of k must be contiguous")
+
+
+def test_workspace_bytes(lib):
+    # decode-shaped paged call needs split partials; small prefill needs none
+    q = desc([64, 32, 128])
+    k = desc([4000, 32, 8, 128])
+    bt = desc([64, 128], dtype=FA_DTYPE_I32)
+    n = fa.fa_varlen_workspace_bytes(q, k, k, 64, bt, 32)
+    assert n > 0 and n % 4 == 0
+    assert fa.fa_varlen_workspace_bytes(Q, K3, K3, 3, None, 0) == 0
+    with pytest.raises(fa.FlashAttnError) as e:
+        fa.fa_varlen_workspace_bytes(Q, K3, desc([86, 2, 32]), 3, None, 0)
+    assert e.value.status == "FA_ERR_SHAPE"

@@ -1,0 +1,56 @@
+"""Build libfa_varlen.so in place with hipcc for gfx950 (no JIT, no cache dir)."""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+LIB = os.path.join(HERE, "libfa_varlen.so")
+SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip")]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found")
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source into the shared library (always recompiles)."""
+    out_tmp = LIB + ".tmp%d" % os.getpid()
+    objs = []
+    try:
+        for src in SOURCES:
+            obj = os.path.join(CSRC, os.path.basename(src) + ".o")
+            cmd = [hipcc(), "-std=c++17", "-O3", "-fPIC", "--offload-arch=" + ARCH,
+                   "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                   "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+                   "-c", src, "-o", obj]
+            if src.endswith(".cpp"):
+                cmd[1:1] = ["-x", "hip"]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            objs.append(obj)
+        cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", out_tmp] + objs
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(out_tmp, LIB)
+    finally:
+        for o in objs:
+            if os.path.exists(o):
+                os.remove(o)
+        if os.path.exists(out_tmp):
+            os.remove(out_tmp)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose="-v" in sys.argv)
+    print(LIB)

@@ -1,0 +1,293 @@
+// Host front end of the C ABI: argument contract, planning, device checks.
+//
+// The contract checks follow candle's FlashAttentionVarLen forward as the
+// error-explainer pages quote it (pages "flash-attn-varlen expects input
+// tensors of rank 3" and "flash-attn-varlen paged expects k/v tensors of rank
+// 4", section Source: ranks then last-dim contiguity; pages "paged flash-attn
+// requires page_block_size" and "... to be a multiple of 32", section Source:
+// the paged shape chain and the non-paged k/v shape check).  The order of the
+// checks and the message texts are kept identical because callers match on
+// them.  Checks the pages do not show (dtypes, out, block table shape, head
+// divisibility, workspace) come after and carry their own texts.
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "../../include/fa_varlen.h"
+#include "fa_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+// Rust-style debug list: [a, b, c]
+std::string dims(const fa_tensor* t, bool strides) {
+    std::string s = "[";
+    for (int i = 0; i < t->rank && i < 4; ++i) {
+        if (i) s += ", ";
+        s += std::to_string(strides ? t->stride[i] : t->shape[i]);
+    }
+    return s + "]";
+}
+
+bool same_dims(const fa_tensor* a, const fa_tensor* b) {
+    if (a->rank != b->rank) return false;
+    for (int i = 0; i < a->rank; ++i)
+        if (a->shape[i] != b->shape[i]) return false;
+    return true;
+}
+
+int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+               int32_t batch, const fa_tensor* bt, int32_t page_block_size) {
+    if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
+    for (const fa_tensor* t : {q, k, v})
+        if (t->rank < 0 || t->rank > 4)
+            return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
+    if (q->dtype != FA_DTYPE_BF16 || k->dtype != FA_DTYPE_BF16 || v->dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_DTYPE, "flash-attn-varlen takes bf16 q/k/v (dtype codes q: %d, k: %d, v: %d)",
+                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
+
+    const bool paged = bt != nullptr;
+    const int q_rank = q->rank, k_rank = k->rank, v_rank = v->rank;
+    if (q_rank != 3 || (!paged && k_rank != 3) || (!paged && v_rank != 3))
+        return fail(FA_ERR_RANK, "flash-attn-varlen expects input tensors of rank 3 (q: %d, k: %d, v: %d",
+                    q_rank, k_rank, v_rank);
+    if (paged && (k_rank != 4 || v_rank != 4))
+        return fail(FA_ERR_RANK, "flash-attn-varlen paged expects k/v tensors of rank 4 (k: %d, v: %d)",
+                    k_rank, v_rank);
+    if (q->stride[q_rank - 1] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of q must be contiguous %s", dims(q, true).c_str());
+    if (k->stride[k_rank - 1] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of k must be contiguous %s", dims(k, true).c_str());
+    if (v->stride[v_rank - 1] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of v must be contiguous %s", dims(v, true).c_str());
+
+    const int64_t total_q = q->shape[0], num_heads = q->shape[1], head_size = q->shape[2];
+    int64_t num_heads_k;
+    if (paged) {
+        const int64_t page = k->shape[1];
+        num_heads_k = k->shape[2];
+        if (!same_dims(k, v))
+            return fail(FA_ERR_SHAPE, "shape mismatch k %s and v %s", dims(k, false).c_str(),
+                        dims(v, false).c_str());
+        if (k->shape[3] != head_size)
+            return fail(FA_ERR_SHAPE, "shape mismatch q %s and k %s", dims(q, false).c_str(),
+                        dims(k, false).c_str());
+        if (page_block_size <= 0) return fail(FA_ERR_PAGE_SIZE, "paged flash-attn requires page_block_size");
+        if ((int64_t)page_block_size != page)
+            return fail(FA_ERR_PAGE_SIZE, "page_block_size %d does not match k shape %s",
+                        (int)page_block_size, dims(k, false).c_str());
+        if (page % 32 != 0)
+            return fail(FA_ERR_PAGE_SIZE,
+                        "paged flash-attn requires page_block_size to be a multiple of 32 (got %lld)",
+                        (long long)page);
+        if (head_size > 512)
+            return fail(FA_ERR_HEAD_DIM, "paged flash-attn supports head sizes up to 512 (got %lld)",
+                        (long long)head_size);
+    } else {
+        num_heads_k = k->shape[1];
+        const int64_t total_k = k->shape[0];
+        if (!(k->shape[0] == total_k && k->shape[1] == num_heads_k && k->shape[2] == head_size))
+            return fail(FA_ERR_SHAPE, "shape mismatch q %s and k %s", dims(q, false).c_str(),
+                        dims(k, false).c_str());
+        if (!(v->shape[0] == total_k && v->shape[1] == num_heads_k && v->shape[2] == head_size))
+            return fail(FA_ERR_SHAPE, "shape mismatch q %s and v %s", dims(q, false).c_str(),
+                        dims(v, false).c_str());
+    }
+
+    // ---- checks beyond the quoted ones
+    if (head_size < 1 || head_size > 512)
+        return fail(FA_ERR_HEAD_DIM, "flash-attn-varlen supports head sizes 1..512 (got %lld)",
+                    (long long)head_size);
+    if (num_heads < 1 || num_heads_k < 1 || num_heads % num_heads_k != 0)
+        return fail(FA_ERR_ARGUMENT,
+                    "number of heads in q (%lld) must be a positive multiple of the number of heads in k/v (%lld)",
+                    (long long)num_heads, (long long)num_heads_k);
+    if (batch < 0) return fail(FA_ERR_ARGUMENT, "batch must be >= 0 (got %d)", (int)batch);
+    if (total_q < 0 || total_q * num_heads >= INT32_MAX)
+        return fail(FA_ERR_ARGUMENT, "total_q * num_heads must be below 2^31 (got %lld * %lld)",
+                    (long long)total_q, (long long)num_heads);
+    for (const fa_tensor* t : {q, k, v})
+        for (int i = 0; i < t->rank; ++i)
+            if (t->shape[i] < 0 || t->stride[i] < 0)
+                return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(t, false).c_str(),
+                            dims(t, true).c_str());
+    if (out) {
+        if (out->dtype != FA_DTYPE_BF16)
+            return fail(FA_ERR_DTYPE, "out must be bf16 (dtype code %d)", (int)out->dtype);
+        if (!same_dims(out, q))
+            return fail(FA_ERR_SHAPE, "out must have the shape of q %s (got %s)", dims(q, false).c_str(),
+                        dims(out, false).c_str());
+        if (out->stride[2] != 1)
+            return fail(FA_ERR_CONTIGUOUS, "the last dim of out must be contiguous %s",
+                        dims(out, true).c_str());
+    }
+    if (paged) {
+        if (bt->dtype != FA_DTYPE_I32)
+            return fail(FA_ERR_DTYPE, "block_table must be int32 (dtype code %d)", (int)bt->dtype);
+        if (bt->rank != 2 || bt->shape[0] != batch || bt->shape[1] < 0)
+            return fail(FA_ERR_SHAPE, "block_table must have shape (batch=%d, max_blocks) (got %s)",
+                        (int)batch, dims(bt, false).c_str());
+        if (bt->stride[1] != 1 && bt->shape[1] > 1)
+            return fail(FA_ERR_CONTIGUOUS, "block_table last dimension must be contiguous");
+        if (bt->shape[1] * (int64_t)page_block_size >= INT32_MAX)
+            return fail(FA_ERR_ARGUMENT, "max_blocks * page_block_size must be below 2^31");
+    } else if (k->shape[0] >= INT32_MAX) {
+        return fail(FA_ERR_ARGUMENT, "total_k must be below 2^31");
+    }
+    return FA_OK;
+}
+
+fa::Shapes shapes_of(const fa_tensor* q, const fa_tensor* k, int32_t batch, const fa_tensor* bt,
+                     int32_t page_block_size) {
+    fa::Shapes s;
+    s.total_q = q->shape[0];
+    s.H = q->shape[1];
+    s.D = q->shape[2];
+    s.paged = bt != nullptr;
+    s.Hk = s.paged ? k->shape[2] : k->shape[1];
+    s.max_lk = s.paged ? bt->shape[1] * (int64_t)page_block_size : k->shape[0];
+    s.batch = batch;
+    return s;
+}
+
+bool is_device_ptr(const void* p) {
+    hipPointerAttribute_t a;
+    if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return a.type == hipMemoryTypeDevice || a.type == hipMemoryTypeManaged;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                    int32_t batch, const fa_tensor* block_table, int32_t page_block_size) {
+    return check_impl(q, k, v, out, batch, block_table, page_block_size);
+}
+
+int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, int32_t batch,
+                              const fa_tensor* block_table, int32_t page_block_size, size_t* bytes) {
+    if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
+    int rc = check_impl(q, k, v, nullptr, batch, block_table, page_block_size);
+    if (rc) return rc;
+    fa::Plan plan;
+    rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
+    if (rc) return fail(rc, "no launch plan for these shapes");
+    *bytes = plan.ws_bytes;
+    return FA_OK;
+}
+
+int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                  const fa_tensor* block_table, int32_t page_block_size, float softmax_scale,
+                  int32_t window_left, int32_t window_right, float* softmax_lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
+    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size);
+    if (rc) return rc;
+    const bool paged = block_table != nullptr;
+    const int64_t total_q = q->shape[0];
+    if (batch == 0 || total_q == 0) return FA_OK;  // nothing to compute, nothing written
+
+    if (!cu_seqlens_q || !is_device_ptr(cu_seqlens_q))
+        return fail(FA_ERR_DEVICE, "seqlens_q must be a cuda tensor");
+    if (!cu_seqlens_k || !is_device_ptr(cu_seqlens_k))
+        return fail(FA_ERR_DEVICE, "seqlens_k must be a cuda tensor");
+    if (paged && (!block_table->data || !is_device_ptr(block_table->data)))
+        return fail(FA_ERR_DEVICE, "block_table must be a cuda tensor");
+    if (!q->data || !is_device_ptr(q->data)) return fail(FA_ERR_DEVICE, "q must be a cuda tensor");
+    if (!k->data || !is_device_ptr(k->data)) return fail(FA_ERR_DEVICE, "k must be a cuda tensor");
+    if (!v->data || !is_device_ptr(v->data)) return fail(FA_ERR_DEVICE, "v must be a cuda tensor");
+    if (!out->data || !is_device_ptr(out->data)) return fail(FA_ERR_DEVICE, "out must be a cuda tensor");
+    if (softmax_lse && !is_device_ptr(softmax_lse))
+        return fail(FA_ERR_DEVICE, "softmax_lse must be a cuda tensor");
+
+    fa::Plan plan;
+    rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
+    if (rc) return fail(rc, "no launch plan for these shapes");
+    if (plan.ws_bytes) {
+        if (!workspace || workspace_bytes < plan.ws_bytes)
+            return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
+        if (!is_device_ptr(workspace)) return fail(FA_ERR_DEVICE, "workspace must be a cuda tensor");
+    }
+
+    fa::FwdParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = static_cast<const uint16_t*>(q->data);
+    p.k = static_cast<const uint16_t*>(k->data);
+    p.v = static_cast<const uint16_t*>(v->data);
+    p.out = static_cast<uint16_t*>(out->data);
+    p.lse = softmax_lse;
+    p.cu_q = cu_seqlens_q;
+    p.cu_k = cu_seqlens_k;
+    p.q_s0 = q->stride[0];
+    p.q_s1 = q->stride[1];
+    p.o_s0 = out->stride[0];
+    p.o_s1 = out->stride[1];
+    if (paged) {
+        p.bt = static_cast<const int32_t*>(block_table->data);
+        p.bt_s0 = block_table->stride[0];
+        p.page = page_block_size;
+        p.k_s0 = k->stride[0]; p.k_s1 = k->stride[1]; p.k_s2 = k->stride[2];
+        p.v_s0 = v->stride[0]; p.v_s1 = v->stride[1]; p.v_s2 = v->stride[2];
+    } else {
+        p.bt = nullptr;
+        p.page = 0;
+        p.k_s0 = k->stride[0]; p.k_s1 = k->stride[1]; p.k_s2 = 0;
+        p.v_s0 = v->stride[0]; p.v_s1 = v->stride[1]; p.v_s2 = 0;
+    }
+    p.batch = batch;
+    p.H = (int32_t)q->shape[1];
+    p.Hk = (int32_t)(paged ? k->shape[2] : k->shape[1]);
+    p.G = p.H / p.Hk;
+    p.D = (int32_t)q->shape[2];
+    p.total_q = (int32_t)total_q;
+    p.window_left = window_left < 0 ? -1 : window_left;
+    p.window_right = window_right < 0 ? -1 : window_right;
+    p.chunk = plan.chunk;
+    p.max_chunks = plan.max_chunks;
+    p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    if (plan.ws_bytes) {
+        const size_t n_o = (size_t)plan.max_chunks * (size_t)total_q * (size_t)p.H * (size_t)plan.dp;
+        p.part_o = static_cast<float*>(workspace);
+        p.part_lse = p.part_o + n_o;
+    }
+    // 16-byte vector access is legal when every row start is 16-byte aligned
+    bool vec = (p.D % 8 == 0);
+    for (const fa_tensor* t : {q, k, v, out}) {
+        vec = vec && aligned16(t->data);
+        for (int i = 0; i + 1 < t->rank; ++i) vec = vec && (t->stride[i] % 8 == 0);
+    }
+    p.vec = vec ? 1 : 0;
+
+    rc = fa::launch_fwd(plan, p, stream);
+    if (rc) return fail(rc, "kernel launch failed: %s", fa::last_hip_error());
+    return FA_OK;
+}
+
+const char* fa_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

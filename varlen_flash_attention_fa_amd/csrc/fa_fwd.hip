@@ -1,0 +1,639 @@
+// gfx950 kernels of the varlen (paged) flash-attention forward, and the host
+// planner that picks their launch shapes.
+//
+// What is computed (the operation named by candle's FlashAttentionVarLen
+// forward; layouts from the pages "flash-attn-varlen expects input tensors of
+// rank 3" and "flash-attn-varlen paged expects k/v tensors of rank 4",
+// sections What it means): for sequence b, query row i, head h,
+//   out[i,h,:] = softmax_j(scale * q[i,h,:] . k_b[j,h/G,:]) v_b[j,h/G,:]
+// over the keys j visible to row i (window around a = i + Lk - Lq).  Paged
+// K/V rows are found through block_table[b][j / P], slot j % P (page
+// "page_block_size ... does not match k shape", section What it means).
+//
+// Work decomposition.  A work item is (sequence b, row tile, key chunk) for one
+// K/V head hk (grid.y).  The rows of (b, hk) are the pairs (query i, head g in
+// the group) numbered r = i*G + g, so one tile packs all G query heads that
+// read the same K/V head and every K/V tile staged in LDS serves all of them.
+// Each wave owns MR rows; the workgroup's WR waves share the K/V tiles.
+//
+// Per wave the scores are computed transposed, S^T = K Q^T, with bf16 MFMA
+// (32x32x16 when MR = 32, 16x16x32 when MR = 16): every lane then holds a
+// single query row, so row max / row sum are in-lane plus one or two
+// cross-lane steps, and the O^T = V^T P^T product takes P straight from the
+// score registers.  The rows of the K operand are fed in a permuted key order
+// chosen so that the eight keys a lane holds in its score registers are
+// exactly the eight keys it must supply as the B operand of the PV MFMA.
+// V is transposed once while being staged into LDS.
+//
+// Online softmax in the log2 domain (scale * log2 e folded in, v_exp_f32),
+// fp32 accumulation, P rounded to bf16 for the PV product, output rounded to
+// bf16 (round to nearest even).  Keys past a tile's end are zero-filled in LDS
+// and masked, so stale or NaN memory is never read.
+//
+// Split-KV: when a sequence's keys are cut into several chunks, each item
+// writes its normalized fp32 partial and log2-sum-exp to the workspace and a
+// second kernel merges them (lse-weighted average).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <climits>
+#include <cstdlib>
+#include <cstring>
+
+#include "../../include/fa_varlen.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kNegInf = -__builtin_huge_valf();
+
+template <int MR>
+struct Mfma;
+template <>
+struct Mfma<32> {
+    static constexpr int KSTEP = 16;  // contraction length per instruction
+    static constexpr int NACC = 16;   // accumulators per lane
+    typedef f32x16 acc_t;
+    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<16> {
+    static constexpr int KSTEP = 32;
+    static constexpr int NACC = 4;
+    typedef f32x4 acc_t;
+    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+};
+
+__device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Eight bf16 at base[d0 .. d0+8), zero past D.  `vec` promises that base is
+// 16-byte aligned whenever d0 is a multiple of 8 and that D % 8 == 0.
+__device__ __forceinline__ u32x4 load8(const uint16_t* base, int d0, int D, bool vec) {
+    if (vec) {
+        if (d0 < D) return *reinterpret_cast<const u32x4*>(base + d0);
+        return u32x4{0u, 0u, 0u, 0u};
+    }
+    unsigned int w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        unsigned int lo = (d0 + 2 * j < D) ? base[d0 + 2 * j] : 0u;
+        unsigned int hi = (d0 + 2 * j + 1 < D) ? base[d0 + 2 * j + 1] : 0u;
+        w[j] = lo | (hi << 16);
+    }
+    return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
+    __bf16 x = static_cast<__bf16>(a);
+    __bf16 y = static_cast<__bf16>(b);
+    return (unsigned int)__builtin_bit_cast(unsigned short, x) |
+           ((unsigned int)__builtin_bit_cast(unsigned short, y) << 16);
+}
+
+__device__ __forceinline__ unsigned short to_bf16(float a) {
+    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(a));
+}
+
+__device__ __forceinline__ float wave_max_xor(float x, int mask) {
+    return fmaxf(x, __shfl_xor(x, mask, 64));
+}
+
+struct Item {
+    int b, rt, c, nc;
+    int q0, Lq, k0, Lk;
+};
+
+// Map a flat work-item index to (sequence, row tile, chunk).  Items are
+// numbered sequence by sequence; sequence b owns ceil(Lq*G/R) row tiles times
+// nc(b) chunks.  Every wave of the workgroup runs this redundantly (no LDS).
+__device__ bool locate(const FwdParams& p, int item, int R, bool split, Item* out) {
+    const int lane = threadIdx.x & 63;
+    int remaining = item;
+    for (int base = 0; base < p.batch; base += 64) {
+        const int b = base + lane;
+        int q0 = 0, lq = 0, k0 = 0, lk = 0, cnt = 0, nc = 1;
+        if (b < p.batch) {
+            q0 = p.cu_q[b];
+            lq = p.cu_q[b + 1] - q0;
+            k0 = p.cu_k[b];
+            lk = p.cu_k[b + 1] - k0;
+            nc = split ? min(p.max_chunks, max(1, ceil_div(lk, p.chunk))) : 1;
+            cnt = ceil_div(lq * p.G, R) * nc;
+        }
+        int incl = cnt;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            int t = __shfl_up(incl, off, 64);
+            if (lane >= off) incl += t;
+        }
+        const int total = __shfl(incl, 63, 64);
+        if (remaining < total) {
+            const unsigned long long hit = __ballot(incl > remaining);
+            const int src = __ffsll((long long)hit) - 1;
+            Item it;
+            it.b = __shfl(b, src, 64);
+            it.q0 = __shfl(q0, src, 64);
+            it.Lq = __shfl(lq, src, 64);
+            it.k0 = __shfl(k0, src, 64);
+            it.Lk = __shfl(lk, src, 64);
+            it.nc = __shfl(nc, src, 64);
+            const int before = __shfl(incl - cnt, src, 64);
+            const int local = remaining - before;
+            it.rt = local / it.nc;
+            it.c = local % it.nc;
+            *out = it;
+            return true;
+        }
+        remaining -= total;
+    }
+    return false;
+}
+
+// Key ranges are [lo, hi) in sequence-local key positions.
+struct Range {
+    int lo, hi;
+};
+
+__device__ __forceinline__ Range row_range(const FwdParams& p, int i, int Lq, int Lk) {
+    const int a = i + Lk - Lq;
+    Range r;
+    r.lo = p.window_left >= 0 ? max(0, a - p.window_left) : 0;
+    r.hi = p.window_right >= 0 ? min(Lk, a + p.window_right + 1) : Lk;
+    return r;
+}
+
+// Element pointer of key row n (sequence-local) of K/V head hk.
+__device__ __forceinline__ const uint16_t* kv_row(const FwdParams& p, const uint16_t* base, int64_t s0,
+                                                  int64_t s1, int64_t s2, const int32_t* bt_row, int k0,
+                                                  int n, int hk) {
+    if (bt_row) {
+        const int blk = bt_row[n / p.page];
+        return base + (int64_t)blk * s0 + (int64_t)(n % p.page) * s1 + (int64_t)hk * s2;
+    }
+    return base + (int64_t)(k0 + n) * s0 + (int64_t)hk * s1;
+}
+
+// Main attention kernel.  DP: padded head dim; MR: rows per wave (MFMA shape);
+// WR: waves per workgroup; BN: keys per LDS tile.
+template <int DP, int MR, int WR, int BN>
+__global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
+    typedef Mfma<MR> M;
+    typedef typename M::acc_t acc_t;
+    constexpr int NT = 64 * WR;
+    constexpr int R = MR * WR;
+    constexpr int KP = DP + 8;   // LDS pitch of K rows (elements); keeps 16-byte alignment
+    constexpr int VP = BN + 8;   // LDS pitch of V^T rows
+    constexpr int NU = BN / 32;  // 32-key units per tile
+    constexpr int NKS = DP / M::KSTEP;
+    constexpr int NDB = DP / MR;  // d-blocks of the O^T accumulator
+    static_assert(BN % 32 == 0, "tile must be whole 32-key units");
+
+    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[DP * VP];
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int hk = blockIdx.y;
+    const bool split = p.max_chunks > 1;
+    const bool vec = p.vec != 0;
+    const int D = p.D;
+
+    Item it;
+    if (!locate(p, blockIdx.x, R, split, &it)) return;
+    if (!split) {  // heaviest (last) row tiles of a causal sequence first
+        const int nrt = ceil_div(it.Lq * p.G, R);
+        it.rt = nrt - 1 - it.rt;
+    }
+    const int Lq = it.Lq, Lk = it.Lk;
+    const int nrows = Lq * p.G;
+    const int32_t* bt_row = p.bt ? p.bt + (int64_t)it.b * p.bt_s0 : nullptr;
+
+    // keys of this item: union of the tile rows' windows, cut to the chunk
+    const int r_first = it.rt * R;
+    const int r_last = min(nrows, r_first + R) - 1;
+    const Range rf = row_range(p, r_first / p.G, Lq, Lk);
+    const Range rl = row_range(p, r_last / p.G, Lq, Lk);
+    int kb = rf.lo, ke = rl.hi;
+    if (split) {
+        kb = max(kb, it.c * p.chunk);
+        ke = min(ke, (it.c + 1) * p.chunk);
+    }
+
+    // this lane's row
+    const int rloc = lane % MR;
+    const int kgrp = lane / MR;
+    const int r = r_first + wave * MR + rloc;
+    const bool row_ok = r < nrows;
+    const int qi = row_ok ? r / p.G : 0;
+    const int g = row_ok ? r % p.G : 0;
+    const int h = hk * p.G + g;
+    int lo = INT_MIN, hi = INT_MAX;
+    if (row_ok) {
+        const Range rr = row_range(p, qi, Lq, Lk);
+        lo = max(rr.lo, kb);
+        hi = min(rr.hi, ke);
+    }
+    // wave-uniform bounds: a tile needs no mask if it lies inside every row's range
+    int w_lo = lo, w_hi = hi;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
+        w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
+    }
+
+    // Q^T operand: lane holds q[row][s*KSTEP + kgrp*8 .. +8) for every k-step s
+    u32x4 qreg[NKS];
+    {
+        const uint16_t* qrow = p.q + (int64_t)(it.q0 + qi) * p.q_s0 + (int64_t)h * p.q_s1;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            qreg[s] = row_ok ? load8(qrow, s * M::KSTEP + kgrp * 8, D, vec) : u32x4{0u, 0u, 0u, 0u};
+    }
+
+    acc_t o[NDB];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v = 0; v < M::NACC; ++v) o[db][v] = 0.f;
+    float m_run = kNegInf, l_run = 0.f;
+    const float c2 = p.scale_log2;
+
+    for (int n0 = kb; n0 < ke; n0 += BN) {
+        __syncthreads();  // previous tile fully consumed
+        // ---- stage K rows [n0, n0+BN) -> sK (row-major), zero past ke
+        {
+            constexpr int CH = DP / 8;  // 16-byte chunks per row
+            for (int idx = threadIdx.x; idx < BN * CH; idx += NT) {
+                const int kr = idx / CH, dc = idx % CH;
+                const int n = n0 + kr;
+                u32x4 val = u32x4{0u, 0u, 0u, 0u};
+                if (n < ke) {
+                    const uint16_t* row = kv_row(p, p.k, p.k_s0, p.k_s1, p.k_s2, bt_row, it.k0, n, hk);
+                    val = load8(row, dc * 8, D, vec);
+                }
+                *reinterpret_cast<u32x4*>(&sK[kr * KP + dc * 8]) = val;
+            }
+        }
+        // ---- stage V rows transposed: sV[d][key], 4 keys x 8 d per step
+        {
+            constexpr int CH = DP / 8;
+            for (int idx = threadIdx.x; idx < (BN / 4) * CH; idx += NT) {
+                const int kg = idx / CH, dc = idx % CH;
+                u32x4 rows4[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int n = n0 + kg * 4 + j;
+                    rows4[j] = u32x4{0u, 0u, 0u, 0u};
+                    if (n < ke) {
+                        const uint16_t* row = kv_row(p, p.v, p.v_s0, p.v_s1, p.v_s2, bt_row, it.k0, n, hk);
+                        rows4[j] = load8(row, dc * 8, D, vec);
+                    }
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    // d = dc*8 + 2w (low halves) and 2w+1 (high halves)
+                    const unsigned a0 = rows4[0][w], a1 = rows4[1][w], a2 = rows4[2][w], a3 = rows4[3][w];
+                    u32x2 even = u32x2{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+                    u32x2 odd = u32x2{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+                    *reinterpret_cast<u32x2*>(&sV[(dc * 8 + 2 * w) * VP + kg * 4]) = even;
+                    *reinterpret_cast<u32x2*>(&sV[(dc * 8 + 2 * w + 1) * VP + kg * 4]) = odd;
+                }
+            }
+        }
+        __syncthreads();
+
+        // ---- S^T = K Q^T for this wave's rows, one accumulator set per 32-key unit
+        constexpr int SPU = MR / 2;  // score values per lane per 32-key unit
+        float sc[NU][SPU];
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if constexpr (MR == 32) {
+                // A row rho holds key u*32 + kappa(rho), kappa swaps bits 2 and 3
+                const int rho = rloc;
+                const int key = u * 32 + ((rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1));
+                const uint16_t* krow = &sK[key * KP + kgrp * 8];
+                acc_t s = {};
+#pragma unroll
+                for (int st = 0; st < NKS; ++st) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(krow + st * 16);
+                    s = M::mma(a, qreg[st], s);
+                }
+#pragma unroll
+                for (int v = 0; v < 16; ++v) sc[u][v] = s[v];
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int rho = rloc;
+                    const int key = u * 32 + (rho >> 2) * 8 + sb * 4 + (rho & 3);
+                    const uint16_t* krow = &sK[key * KP + kgrp * 8];
+                    acc_t s = {};
+#pragma unroll
+                    for (int st = 0; st < NKS; ++st) {
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + st * 32);
+                        s = M::mma(a, qreg[st], s);
+                    }
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) sc[u][sb * 4 + v] = s[v];
+                }
+            }
+        }
+
+        // ---- scale, mask, running max
+        const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
+        float mx = kNegInf;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int e = 0; e < SPU; ++e) {
+                float t = sc[u][e] * c2;
+                if (need_mask) {
+                    // key held by value e of unit u in this lane
+                    int key;
+                    if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
+                    else key = u * 32 + kgrp * 8 + e;
+                    const int n = n0 + key;
+                    if (n < lo || n >= hi) t = kNegInf;
+                }
+                sc[u][e] = t;
+                mx = fmaxf(mx, t);
+            }
+        if constexpr (MR == 32) {
+            mx = wave_max_xor(mx, 32);
+        } else {
+            mx = wave_max_xor(mx, 16);
+            mx = wave_max_xor(mx, 32);
+        }
+        const float m_new = fmaxf(m_run, mx);
+        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float rs = 0.f;
+        unsigned int pk[NU][SPU / 2];
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int e = 0; e < SPU; e += 2) {
+                const float p0 = __builtin_amdgcn_exp2f(sc[u][e] - m_use);
+                const float p1 = __builtin_amdgcn_exp2f(sc[u][e + 1] - m_use);
+                rs += p0 + p1;
+                pk[u][e / 2] = pack_bf16x2(p0, p1);
+            }
+        if constexpr (MR == 32) {
+            rs += __shfl_xor(rs, 32, 64);
+        } else {
+            rs += __shfl_xor(rs, 16, 64);
+            rs += __shfl_xor(rs, 32, 64);
+        }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v = 0; v < M::NACC; ++v) o[db][v] *= alpha;
+
+        // ---- O^T += V^T P^T
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+            if constexpr (MR == 32) {
+#pragma unroll
+                for (int ts = 0; ts < 2; ++ts) {
+                    const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
+                                          pk[u][ts * 4 + 3]};
+                    const int kcol = u * 32 + ts * 16 + kgrp * 8;
+#pragma unroll
+                    for (int db = 0; db < NDB; ++db) {
+                        const u32x4 a =
+                            *reinterpret_cast<const u32x4*>(&sV[(db * 32 + rloc) * VP + kcol]);
+                        o[db] = M::mma(a, b, o[db]);
+                    }
+                }
+            } else {
+                const u32x4 b = u32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
+                const int kcol = u * 32 + kgrp * 8;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db) {
+                    const u32x4 a = *reinterpret_cast<const u32x4*>(&sV[(db * 16 + rloc) * VP + kcol]);
+                    o[db] = M::mma(a, b, o[db]);
+                }
+            }
+        }
+    }
+
+    // ---- epilogue
+    if (!row_ok) return;
+    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float lse2 = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : kNegInf;
+    const int t = it.q0 + qi;
+    if (split && it.nc > 1) {
+        float* po = p.part_o + (((int64_t)it.c * p.total_q + t) * p.H + h) * DP;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+#pragma unroll
+            for (int v4 = 0; v4 < M::NACC; v4 += 4) {
+                int d;
+                if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
+                else d = db * 16 + kgrp * 4;
+                f32x4 val = {o[db][v4] * inv, o[db][v4 + 1] * inv, o[db][v4 + 2] * inv,
+                             o[db][v4 + 3] * inv};
+                *reinterpret_cast<f32x4*>(po + d) = val;
+            }
+        if (kgrp == 0) p.part_lse[((int64_t)it.c * p.total_q + t) * p.H + h] = lse2;
+        return;
+    }
+    uint16_t* orow = p.out + (int64_t)t * p.o_s0 + (int64_t)h * p.o_s1;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int v4 = 0; v4 < M::NACC; v4 += 4) {
+            int d;
+            if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
+            else d = db * 16 + kgrp * 4;
+            if (d >= D) continue;
+            const float x0 = o[db][v4] * inv, x1 = o[db][v4 + 1] * inv;
+            const float x2 = o[db][v4 + 2] * inv, x3 = o[db][v4 + 3] * inv;
+            if (vec) {
+                *reinterpret_cast<u32x2*>(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+            } else {
+                const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (d + j < D) orow[d + j] = to_bf16(xs[j]);
+            }
+        }
+    if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.total_q + t] = lse2 * 0.6931471805599453f;
+}
+
+// Merge split partials: one wave per (token, head).
+template <int DP>
+__global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
+    const int lane = threadIdx.x & 63;
+    const int t = blockIdx.x;
+    const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
+    if (h >= p.H) return;
+    // sequence of token t: last b with cu_q[b] <= t
+    int lo = 0, hi = p.batch;  // answer in [0, batch)
+    if (t >= p.cu_q[p.batch]) return;
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (p.cu_q[mid] <= t) lo = mid; else hi = mid;
+    }
+    const int b = lo;
+    const int Lk = p.cu_k[b + 1] - p.cu_k[b];
+    const int nc = min(p.max_chunks, max(1, ceil_div(Lk, p.chunk)));
+    if (nc <= 1) return;
+    const float* pl = p.part_lse + (int64_t)t * p.H + h;
+    const int64_t cstride_l = (int64_t)p.total_q * p.H;
+    float M = kNegInf;
+    for (int c = lane; c < nc; c += 64) M = fmaxf(M, pl[c * cstride_l]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    uint16_t* orow = p.out + (int64_t)t * p.o_s0 + (int64_t)h * p.o_s1;
+    const int D = p.D;
+    if (M == kNegInf) {  // no chunk saw a key
+        for (int d = lane; d < D; d += 64) orow[d] = 0;
+        if (p.lse && lane == 0) p.lse[(int64_t)h * p.total_q + t] = kNegInf;
+        return;
+    }
+    constexpr int PER = DP / 64;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+    float wsum = 0.f;
+    const float* po = p.part_o + ((int64_t)t * p.H + h) * DP;
+    const int64_t cstride_o = (int64_t)p.total_q * p.H * DP;
+    for (int c = 0; c < nc; ++c) {
+        const float w = __builtin_amdgcn_exp2f(pl[c * cstride_l] - M);
+        wsum += w;
+        if (w == 0.f) continue;
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] += w * po[c * cstride_o + j * 64 + lane];
+    }
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int d = j * 64 + lane;
+        if (d < D) orow[d] = to_bf16(acc[j] * inv);
+    }
+    if (p.lse && lane == 0)
+        p.lse[(int64_t)h * p.total_q + t] = (M + __builtin_amdgcn_logf(wsum)) * 0.6931471805599453f;
+}
+
+hipError_t g_last = hipSuccess;
+
+template <int DP, int MR, int WR, int BN>
+hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
+    dim3 grid((unsigned)plan.grid_x, (unsigned)p.Hk);
+    hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN>), grid, dim3(64 * WR), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DP>
+hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
+    if (plan.kind == KIND_PREFILL) {
+        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64>(plan, p, s);
+        else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32>(plan, p, s);
+        else return launch_attn<DP, 16, 4, 32>(plan, p, s);
+    }
+    // decode: 16 rows per wave, split keys over workgroups
+    if (plan.wr == 1) {
+        if constexpr (DP <= 256) return launch_attn<DP, 16, 1, 32>(plan, p, s);
+        else return launch_attn<DP, 16, 1, 32>(plan, p, s);
+    }
+    return launch_attn<DP, 16, 4, 32>(plan, p, s);
+}
+
+template <int DP>
+hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
+    dim3 grid((unsigned)p.total_q, (unsigned)((p.H + 3) / 4));
+    hipLaunchKernelGGL((combine_kernel<DP>), grid, dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+int env_int(const char* name, int dflt) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::atoi(s);
+}
+
+}  // namespace
+
+const char* last_hip_error() { return hipGetErrorString(g_last); }
+
+int make_plan(const Shapes& s, Plan* plan) {
+    Plan P;
+    std::memset(&P, 0, sizeof P);
+    P.dp = s.D <= 64 ? 64 : s.D <= 128 ? 128 : s.D <= 256 ? 256 : 512;
+    const int64_t G = s.H / s.Hk;
+    const int64_t batch = std::max<int64_t>(1, s.batch);
+    const int64_t rows_avg = (s.total_q * G + batch - 1) / batch;  // rows per (sequence, kv head)
+    int kind = rows_avg <= 64 ? KIND_DECODE : KIND_PREFILL;
+    const char* force = std::getenv("FA_FORCE_PATH");
+    if (force && std::strcmp(force, "prefill") == 0) kind = KIND_PREFILL;
+    if (force && std::strcmp(force, "decode") == 0) kind = KIND_DECODE;
+    P.kind = kind;
+    if (kind == KIND_PREFILL) {
+        P.mr = P.dp <= 256 ? 32 : 16;
+        P.wr = 4;
+        P.bn = P.dp <= 128 ? 64 : 32;
+        P.chunk = INT_MAX;
+        P.max_chunks = 1;
+    } else {
+        P.mr = 16;
+        P.wr = rows_avg <= 16 ? 1 : 4;
+        P.bn = 32;
+        int chunk = P.dp <= 128 ? 256 : P.dp == 256 ? 512 : 1024;
+        chunk = env_int("FA_SPLIT_KEYS", chunk);
+        if (chunk < P.bn) chunk = P.bn;
+        chunk = (chunk + P.bn - 1) / P.bn * P.bn;
+        P.chunk = chunk;
+        const int64_t mc = std::max<int64_t>(1, (s.max_lk + chunk - 1) / chunk);
+        if (mc > 4096) return FA_ERR_ARGUMENT;
+        P.max_chunks = (int)mc;
+        if (P.max_chunks == 1) P.chunk = INT_MAX;
+    }
+    P.rows = P.mr * P.wr;
+    const int64_t tiles = (s.total_q * G + P.rows - 1) / P.rows + s.batch;
+    const int64_t gx = tiles * P.max_chunks;
+    if (gx >= INT32_MAX || s.Hk > 65535) return FA_ERR_ARGUMENT;
+    P.grid_x = gx;
+    P.ws_bytes = P.max_chunks > 1
+                     ? (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * (size_t)(P.dp + 1) * 4u
+                     : 0;
+    *plan = P;
+    return 0;
+}
+
+int launch_fwd(const Plan& plan, const FwdParams& p, void* stream) {
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    switch (plan.dp) {
+        case 64: e = launch_dp<64>(plan, p, s); break;
+        case 128: e = launch_dp<128>(plan, p, s); break;
+        case 256: e = launch_dp<256>(plan, p, s); break;
+        default: e = launch_dp<512>(plan, p, s); break;
+    }
+    if (e == hipSuccess && plan.max_chunks > 1) {
+        switch (plan.dp) {
+            case 64: e = launch_combine<64>(p, s); break;
+            case 128: e = launch_combine<128>(p, s); break;
+            case 256: e = launch_combine<256>(p, s); break;
+            default: e = launch_combine<512>(p, s); break;
+        }
+    }
+    g_last = e;
+    return e == hipSuccess ? 0 : FA_ERR_HIP;
+}
+
+}  // namespace fa

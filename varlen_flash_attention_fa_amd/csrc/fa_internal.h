@@ -1,0 +1,63 @@
+// Internal interface between the host front end (fa_api.cpp) and the kernels
+// (fa_fwd.hip).  Not installed; the public ABI is include/fa_varlen.h.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Everything a kernel launch needs.  Strides are in elements.
+struct FwdParams {
+    const uint16_t* q;      // bf16 bits
+    const uint16_t* k;
+    const uint16_t* v;
+    uint16_t* out;
+    float* lse;             // [H][total_q] natural log, or nullptr
+    const int32_t* cu_q;
+    const int32_t* cu_k;
+    const int32_t* bt;      // block table, nullptr = non-paged
+    float* part_o;          // split partials [chunk][total_q][H][DP] (fp32, normalized)
+    float* part_lse;        // [chunk][total_q][H] log2-domain
+    int64_t q_s0, q_s1;     // token, head
+    int64_t k_s0, k_s1, k_s2;  // paged: block, slot, head; non-paged: token, head, -
+    int64_t v_s0, v_s1, v_s2;
+    int64_t o_s0, o_s1;
+    int64_t bt_s0;
+    int32_t batch, H, Hk, G, D, page;
+    int32_t total_q;
+    int32_t window_left, window_right;
+    int32_t chunk;          // keys per split (split only if max_chunks > 1)
+    int32_t max_chunks;
+    int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
+    float scale_log2;       // softmax_scale * log2(e)
+};
+
+enum Kind { KIND_PREFILL = 0, KIND_DECODE = 1 };
+
+struct Plan {
+    int kind;       // Kind
+    int dp;         // padded head dim: 64/128/256/512
+    int mr;         // MFMA rows per wave (16 or 32)
+    int wr;         // waves per workgroup (each owns mr rows)
+    int bn;         // keys per LDS tile
+    int rows;       // rows per workgroup = mr * wr
+    int chunk;      // keys per split
+    int max_chunks; // upper bound of splits per sequence
+    int64_t grid_x; // workgroups along x (upper bound of work items)
+    size_t ws_bytes;
+};
+
+// Shapes the planner needs (host values only).
+struct Shapes {
+    int64_t total_q, H, Hk, D;
+    int64_t max_lk;     // upper bound of any sequence's key count
+    int64_t batch;
+    bool paged;
+};
+
+int make_plan(const Shapes& s, Plan* plan);   // 0 or an fa_status code
+int launch_fwd(const Plan& plan, const FwdParams& p, void* stream);  // 0 or FA_ERR_HIP
+const char* last_hip_error();
+
+}  // namespace fa
