@@ -1,0 +1,361 @@
+#!/usr/bin/env python3
+"""Benchmark of the varlen (paged) flash-attention forward on one MI355X.
+
+One step = one ``fa_varlen_fwd`` call (every kernel of the path) over one batch
+of seeded synthetic inputs already resident in HBM.  The default workload is
+the paged decode batch (64 sequences, q_len 1, kv lens U[1,4096], page 32,
+H 32 / Hk 8, head_dim 128), reported as KV GB/s; ``--workload`` selects the
+others (prefill ones are reported as TFLOP/s).
+
+Timed region: W untimed warm-up steps, then exactly K steps bracketed by
+``torch.cuda.synchronize()``.  Consecutive steps read different copies of the
+inputs (enough copies to exceed the 256 MB last-level cache), so K/V really
+come from HBM.  The main kernel's own duration is read live with HIP events
+that the library records around it on its launch stream
+(``fa_varlen_set_kernel_events``).
+
+Prints ONE JSON line: metric/value/unit, ms_per_step, a ``roofline`` object
+for the main kernel (algorithmic bytes or FLOP per launch / its mean duration
+vs. the chip's peak) and a ``cpu_baseline`` object (the fp64 oracle timed on a
+bounded sample of the same workload on this host's cores).
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+METRIC = "varlen paged attention: prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)"
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+DECODE = {"c2", "c5a", "c5b"}
+KERNEL_SRC = os.path.join(ROOT, "varlen_flash_attention_fa_amd", "csrc", "fa_fwd.hip")
+
+
+# ------------------------------------------------------------------ HIP events
+
+class Hip:
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        assert rc == 0, rc
+        return e.value
+
+    def record(self, ev, stream):
+        rc = self.lib.hipEventRecord(ev, stream)
+        assert rc == 0, rc
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        assert rc == 0, rc
+        return float(ms.value)
+
+    def destroy(self, ev):
+        self.lib.hipEventDestroy(ev)
+
+
+# ------------------------------------------------------------ algorithmic work
+
+def visible_pairs(lq, lk, wl, wr):
+    """Number of (query, key) pairs visible under the bottom-right aligned window."""
+    total = 0
+    per_seq = []
+    for Lq, Lk in zip(lq, lk):
+        i = np.arange(int(Lq), dtype=np.int64)
+        a = i + int(Lk) - int(Lq)
+        lo = np.maximum(0, a - wl) if wl >= 0 else np.zeros_like(a)
+        hi = np.minimum(int(Lk), a + wr + 1) if wr >= 0 else np.full_like(a, int(Lk))
+        n = np.maximum(0, hi - lo)
+        per_seq.append(n)
+        total += int(n.sum())
+    return total, per_seq
+
+
+def work_of(wl):
+    H, Hk, D = wl.num_heads, wl.num_heads_k, wl.head_dim
+    pairs, per_seq = visible_pairs(wl.lens_q, wl.lens_k, wl.window_left, wl.window_right)
+    flops = 4.0 * D * H * pairs
+    kv_bytes = 2.0 * Hk * D * 2 * float(wl.lens_k.sum())
+    qo_bytes = 2.0 * float(wl.lens_q.sum()) * H * D * 2
+    bt_bytes = 0.0
+    if wl.paged:
+        P = wl.page_block_size
+        bt_bytes = 4.0 * float(((wl.lens_k + P - 1) // P).sum())
+    meta = 8.0 * (wl.batch + 1)
+    return dict(pairs=pairs, per_seq=per_seq, flops=flops, kv_bytes=kv_bytes,
+                total_bytes=kv_bytes + qo_bytes + bt_bytes + meta)
+
+
+# ------------------------------------------------------------------- profiles
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+    path = os.path.join(ROOT, "profiles", "attn_fwd_%s_hbm_traffic.md" % workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel source sha256/16") != kernel_sha():
+        return None
+    try:
+        return float(vals["HBM bytes per launch (scaled)"])
+    except (KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- CPU leg
+
+def cpu_baseline(wl, work, decode: bool):
+    """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
+    import oracle
+    oracle.build()
+    threads = oracle.default_threads()
+    H, D = wl.num_heads, wl.head_dim
+    fma_per_pair = 2.0 * D * H           # q.k and p.v, per head
+    # the oracle runs ~0.4 G fp64 multiply-adds per second per thread: this bounds
+    # the sample to roughly 10 s of wall time on the host cores
+    budget = 4.0e9 * threads
+    if decode:
+        # whole sequences until the budget: metric is KV bytes of the sequences served
+        order = list(range(wl.batch))
+        sel = np.zeros(wl.q.shape[0], np.uint8)
+        kv = 0.0
+        spent = 0.0
+        nseq = 0
+        for b in order:
+            cost = float(work["per_seq"][b].sum()) * fma_per_pair
+            if nseq and spent + cost > budget:
+                break
+            q0, q1 = int(wl.cu_seqlens_q[b]), int(wl.cu_seqlens_q[b + 1])
+            sel[q0:q1] = 1
+            kv += 2.0 * wl.num_heads_k * D * 2 * float(wl.lens_k[b])
+            spent += cost
+            nseq += 1
+        reps, t0 = 0, time.perf_counter()
+        while True:  # repeat a small sample until the timing is at least ~3 s long
+            oracle.attention_workload(wl, token_sel=sel, nthreads=threads)
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= 3.0:
+                break
+        return {"value": round(reps * kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+                "kind": "oracle",
+                "sample": "%d of %d sequences (all their query rows), %.3g GB of K/V, run %d times "
+                          "in %.2f s" % (nseq, wl.batch, kv / 1e9, reps, dt)}
+    # prefill: a seeded sample of query rows; metric is FLOP of those rows
+    rng = np.random.Generator(np.random.PCG64(4242))
+    rows_pairs = np.concatenate(work["per_seq"]).astype(np.float64)
+    T = rows_pairs.shape[0]
+    perm = rng.permutation(T)
+    cum = np.cumsum(rows_pairs[perm] * fma_per_pair)
+    n = int(max(1, min(T, np.searchsorted(cum, budget) + 1)))
+    sel = np.zeros(T, np.uint8)
+    sel[perm[:n]] = 1
+    flops = 4.0 * D * H * float(rows_pairs[perm[:n]].sum())
+    t0 = time.perf_counter()
+    oracle.attention_workload(wl, token_sel=sel, nthreads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d query rows (seeded), %.3g GFLOP, %.2f s" % (n, T, flops / 1e9, dt)}
+
+
+# ---------------------------------------------------------------------- main
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
+              "(no multi-GPU sharding is built)" % args.gpus, file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+    import varlen_flash_attention_fa_amd as fa
+    import workloads as W
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return 0
+
+    fa.load()
+    hip = Hip()
+    print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
+    wl = W.make_config(args.workload, args.seed)
+    work = work_of(wl)
+    decode = args.workload in DECODE
+
+    # enough input copies that consecutive steps do not hit in the 256 MB MALL
+    per_copy = (wl.k.numel() + wl.v.numel() + 2 * wl.q.numel()) * 2
+    ncopies = int(min(8, max(1, math.ceil(2.0e9 / per_copy))))
+    with torch.cuda.stream(stream):
+        copies = []
+        for c in range(ncopies):
+            d = dict(q=wl.q.to(dev), k=wl.k.to(dev), v=wl.v.to(dev),
+                     cu_q=torch.from_numpy(wl.cu_seqlens_q).to(dev),
+                     cu_k=torch.from_numpy(wl.cu_seqlens_k).to(dev),
+                     bt=None if wl.block_table is None else torch.from_numpy(wl.block_table).to(dev))
+            d["out"] = torch.empty_like(d["q"])
+            copies.append(d)
+        torch.cuda.synchronize()
+
+    def descs(d):
+        dq, dk, dv, do = (fa._tdesc(d["q"]), fa._tdesc(d["k"]), fa._tdesc(d["v"]),
+                          fa._tdesc(d["out"]))
+        dbt = fa._tdesc(d["bt"]) if d["bt"] is not None else None
+        return dq, dk, dv, do, dbt
+
+    calls = []
+    ws_bytes = 0
+    for d in copies:
+        dq, dk, dv, do, dbt = descs(d)
+        ws_bytes = fa.fa_varlen_workspace_bytes(dq, dk, dv, wl.batch, dbt, wl.page_block_size)
+        calls.append((dq, dk, dv, do, dbt, d))
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+
+    def step(i, ev_k=None):
+        dq, dk, dv, do, dbt, d = calls[i % ncopies]
+        if ev_k is not None:
+            fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
+        rc = fa.fa_varlen_fwd(dq, dk, dv, do, d["cu_q"].data_ptr(), d["cu_k"].data_ptr(), wl.batch,
+                              dbt, wl.page_block_size, wl.softmax_scale, wl.window_left,
+                              wl.window_right, 0, workspace.data_ptr() if ws_bytes else 0,
+                              ws_bytes, sh)
+        if rc:
+            raise RuntimeError(fa.fa_last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_call = [(hip.event(), hip.event()) for _ in range(K)]
+    ev_kern = [(hip.event(), hip.event()) for _ in range(K)]
+    print("bench: timing %d steps" % K, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        hip.record(ev_call[i][0], sh)
+        step(i, ev_kern[i])
+        hip.record(ev_call[i][1], sh)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fa.fa_varlen_set_kernel_events(0, 0)
+
+    ms_per_step = (t1 - t0) * 1e3 / K
+    call_ms = np.array([hip.elapsed_ms(a, b) for a, b in ev_call])
+    kern_ms = np.array([hip.elapsed_ms(a, b) for a, b in ev_kern])
+    for a, b in ev_call + ev_kern:
+        hip.destroy(a)
+        hip.destroy(b)
+    kern_mean = float(kern_ms.mean())
+
+    if decode:
+        value = work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
+        unit = "GB/s"
+        achieved = work["total_bytes"] / (kern_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        value = work["flops"] / (ms_per_step * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        achieved = work["flops"] / (kern_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    traffic = stored_traffic(args.workload)
+    roof["traffic"] = traffic
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, work, decode)
+
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, seed %d)" % wl.seed,
+        "config": {
+            "workload": "%s: %s" % (args.workload, wl.extra.get("desc", "")),
+            "batch": wl.batch, "total_q": int(wl.lens_q.sum()), "total_k": int(wl.lens_k.sum()),
+            "num_heads": wl.num_heads, "num_heads_k": wl.num_heads_k, "head_dim": wl.head_dim,
+            "page_block_size": wl.page_block_size, "window_left": wl.window_left,
+            "window_right": wl.window_right, "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {
+            "main_kernel_ms_mean": round(kern_mean, 5),
+            "main_kernel_ms_p50": round(float(np.median(kern_ms)), 5),
+            "call_ms_p10_p50_p90": [round(float(np.percentile(call_ms, q)), 5) for q in (10, 50, 90)],
+            "algorithmic_flop": work["flops"], "algorithmic_kv_bytes": work["kv_bytes"],
+            "algorithmic_total_bytes": work["total_bytes"], "visible_pairs_per_head": work["pairs"],
+            "tflops_per_step": round(work["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
+            "kv_gbs_per_step": round(work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9, 2),
+            "input_copies_rotated": ncopies, "workspace_bytes": ws_bytes,
+            "kernel_source_sha256_16": kernel_sha(), "device": props.name,
+            "cus": props.multi_processor_count,
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -136,6 +136,17 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                   int32_t window_right, float* softmax_lse, void* workspace,
                   size_t workspace_bytes, void* stream);
 
+/*
+ * fa_varlen_set_kernel_events -- measurement hook for benchmarks.  With both
+ * arguments non-NULL (hipEvent_t handles created by the caller), every later
+ * fa_varlen_fwd on this thread records `start_event` immediately before and
+ * `stop_event` immediately after its main attention kernel, on the call's
+ * stream, so the caller can read that kernel's duration with
+ * hipEventElapsedTime.  NULL, NULL turns it off.  The events stay owned by the
+ * caller.  Always returns FA_OK.
+ */
+int fa_varlen_set_kernel_events(void* start_event, void* stop_event);
+
 /* Text of the last non-zero status returned on this thread ("" if none). */
 const char* fa_last_error(void);
 

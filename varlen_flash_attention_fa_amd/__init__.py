@@ -19,6 +19,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "FaTensor", "FlashAttnError", "lib_path", "load", "fa_varlen_check",
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
+    "fa_varlen_set_kernel_events",
     "FA_DTYPE_BF16", "FA_DTYPE_I32", "STATUS",
 ]
 
@@ -72,6 +73,8 @@ def load():
                                   ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_varlen_fwd.restype = ctypes.c_int
+    lib.fa_varlen_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_varlen_set_kernel_events.restype = ctypes.c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -142,6 +145,11 @@ def fa_varlen_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqle
                                 int(page_block_size or 0), float(softmax_scale), int(window_left),
                                 int(window_right), softmax_lse or None, workspace or None,
                                 int(workspace_bytes), stream or None)
+
+
+def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:
+    """Measurement hook: bracket the main kernel of later calls with these hipEvent_t handles."""
+    return load().fa_varlen_set_kernel_events(start_event or None, stop_event or None)
 
 
 def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,

@@ -24,6 +24,8 @@
 namespace {
 
 thread_local std::string g_err;
+thread_local void* g_ev_start = nullptr;
+thread_local void* g_ev_stop = nullptr;
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -283,8 +285,18 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     }
     p.vec = vec ? 1 : 0;
 
-    rc = fa::launch_fwd(plan, p, stream);
+    rc = fa::launch_fwd(plan, p, stream, g_ev_start, g_ev_stop);
     if (rc) return fail(rc, "kernel launch failed: %s", fa::last_hip_error());
+    return FA_OK;
+}
+
+int fa_varlen_set_kernel_events(void* start_event, void* stop_event) {
+    if (start_event && stop_event) {
+        g_ev_start = start_event;
+        g_ev_stop = stop_event;
+    } else {
+        g_ev_start = g_ev_stop = nullptr;
+    }
     return FA_OK;
 }
 

@@ -615,15 +615,18 @@ int make_plan(const Shapes& s, Plan* plan) {
     return 0;
 }
 
-int launch_fwd(const Plan& plan, const FwdParams& p, void* stream) {
+int launch_fwd(const Plan& plan, const FwdParams& p, void* stream, void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
+    hipError_t e = hipSuccess;
+    if (ev_start) e = hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
+    if (e != hipSuccess) { g_last = e; return FA_ERR_HIP; }
     switch (plan.dp) {
         case 64: e = launch_dp<64>(plan, p, s); break;
         case 128: e = launch_dp<128>(plan, p, s); break;
         case 256: e = launch_dp<256>(plan, p, s); break;
         default: e = launch_dp<512>(plan, p, s); break;
     }
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(static_cast<hipEvent_t>(ev_stop), s);
     if (e == hipSuccess && plan.max_chunks > 1) {
         switch (plan.dp) {
             case 64: e = launch_combine<64>(p, s); break;

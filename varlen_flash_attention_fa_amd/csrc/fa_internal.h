@@ -57,7 +57,8 @@ struct Shapes {
 };
 
 int make_plan(const Shapes& s, Plan* plan);   // 0 or an fa_status code
-int launch_fwd(const Plan& plan, const FwdParams& p, void* stream);  // 0 or FA_ERR_HIP
+// 0 or FA_ERR_HIP.  ev_start/ev_stop (hipEvent_t or null) bracket the main kernel.
+int launch_fwd(const Plan& plan, const FwdParams& p, void* stream, void* ev_start, void* ev_stop);
 const char* last_hip_error();
 
 }  // namespace fa
