@@ -175,34 +175,70 @@ __device__ __forceinline__ Range row_range(const FwdParams& p, int i, int Lq, in
     return r;
 }
 
-// Element pointer of key row n (sequence-local) of K/V head hk.
-__device__ __forceinline__ const uint16_t* kv_row(const FwdParams& p, const uint16_t* base, int64_t s0,
-                                                  int64_t s1, int64_t s2, const int32_t* bt_row, int k0,
-                                                  int n, int hk) {
-    if (bt_row) {
-        const int blk = bt_row[n / p.page];
-        return base + (int64_t)blk * s0 + (int64_t)(n % p.page) * s1 + (int64_t)hk * s2;
-    }
-    return base + (int64_t)(k0 + n) * s0 + (int64_t)hk * s1;
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    constexpr int n = N > 63 ? 63 : N;
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Main attention kernel.  DP: padded head dim; MR: rows per wave (MFMA shape);
-// WR: waves per workgroup; BN: keys per LDS tile.
-template <int DP, int MR, int WR, int BN>
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// if source lane a points at four consecutive bf16 of row (key0 + a/4),
+// columns d0 + 4*(a%4) .. +3, then lane i receives column d0 + i of rows
+// key0 .. key0+3: a 4-key slice of V^T.
+__device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* ptr) {
+    s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(ptr));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
+// data lands at lds_base + 16*l.  lds_base must be wave-uniform.
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* gsrc, unsigned char* lds_base) {
+    __builtin_amdgcn_global_load_lds((const void*)gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+
+constexpr int kPageCap = 256;
+
+// The lane id laundered through an empty asm: values derived from it inside a
+// loop are recomputed each iteration instead of being hoisted and kept live
+// (keeps register pressure of the unrolled LDS address patterns down).
+__device__ __forceinline__ int opaque_lane() {
+    int l = threadIdx.x & 63;
+    asm volatile("" : "+v"(l));
+    return l;
+}  // block-table entries staged in LDS per segment
+
+// Main attention kernel.
+//   DP: head dim padded to 64/128/256/512      MR: rows per wave (MFMA 32x32x16 or 16x16x32)
+//   WR: waves per workgroup (they share K/V)    BN: keys per tile     NS: LDS pipeline stages
+//
+// K and V tiles live in LDS row-major ([key][d], DP*2 bytes per row) with the
+// 16-byte chunks of row r stored at position (chunk ^ swizzle(r)), so that the
+// MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
+// rows outside [kb, ke) are loaded from the nearest valid row and masked.
+template <int DP, int MR, int WR, int BN, int NS>
 __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR> M;
     typedef typename M::acc_t acc_t;
     constexpr int NT = 64 * WR;
     constexpr int R = MR * WR;
-    constexpr int KP = DP + 8;   // LDS pitch of K rows (elements); keeps 16-byte alignment
-    constexpr int VP = BN + 8;   // LDS pitch of V^T rows
-    constexpr int NU = BN / 32;  // 32-key units per tile
+    constexpr int CH = DP / 8;            // 16-byte chunks per row
+    constexpr int ROWB = DP * 2;          // bytes per LDS row
+    constexpr int TILEB = BN * ROWB;      // bytes per K (or V) tile
+    constexpr int NI = BN * CH / NT;      // 16-byte copies per thread per tensor per tile
+    constexpr int NU = BN / 32;           // 32-key units per tile
     constexpr int NKS = DP / M::KSTEP;
-    constexpr int NDB = DP / MR;  // d-blocks of the O^T accumulator
-    static_assert(BN % 32 == 0, "tile must be whole 32-key units");
+    constexpr int NDB = DP / MR;
+    constexpr int SWK = (CH < 16 ? CH : 16) - 1;
+    constexpr int SWV = (CH < 16 ? CH : 16) - 1;
+    constexpr int RPI = 64 / CH > 0 ? 64 / CH : 1;   // rows per 64-lane copy
+    static_assert(BN % 32 == 0 && (BN * CH) % NT == 0 && CH <= 64 && 64 % CH == 0, "tile shape");
 
-    __shared__ __attribute__((aligned(16))) uint16_t sK[BN * KP];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[DP * VP];
+    __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * 2 * TILEB];
+    __shared__ int s_pages[kPageCap];
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -210,6 +246,8 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
     const bool split = p.max_chunks > 1;
     const bool vec = p.vec != 0;
     const int D = p.D;
+    const bool paged = p.bt != nullptr;
+    const int P = p.page;
 
     Item it;
     if (!locate(p, blockIdx.x, R, split, &it)) return;
@@ -219,7 +257,7 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
     }
     const int Lq = it.Lq, Lk = it.Lk;
     const int nrows = Lq * p.G;
-    const int32_t* bt_row = p.bt ? p.bt + (int64_t)it.b * p.bt_s0 : nullptr;
+    const int32_t* bt_row = paged ? p.bt + (int64_t)it.b * p.bt_s0 : nullptr;
 
     // keys of this item: union of the tile rows' windows, cut to the chunk
     const int r_first = it.rt * R;
@@ -246,7 +284,6 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
         lo = max(rr.lo, kb);
         hi = min(rr.hi, ke);
     }
-    // wave-uniform bounds: a tile needs no mask if it lies inside every row's range
     int w_lo = lo, w_hi = hi;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -271,161 +308,243 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
     float m_run = kNegInf, l_run = 0.f;
     const float c2 = p.scale_log2;
 
-    for (int n0 = kb; n0 < ke; n0 += BN) {
-        __syncthreads();  // previous tile fully consumed
-        // ---- stage K rows [n0, n0+BN) -> sK (row-major), zero past ke
-        {
-            constexpr int CH = DP / 8;  // 16-byte chunks per row
-            for (int idx = threadIdx.x; idx < BN * CH; idx += NT) {
-                const int kr = idx / CH, dc = idx % CH;
-                const int n = n0 + kr;
-                u32x4 val = u32x4{0u, 0u, 0u, 0u};
-                if (n < ke) {
-                    const uint16_t* row = kv_row(p, p.k, p.k_s0, p.k_s1, p.k_s2, bt_row, it.k0, n, hk);
-                    val = load8(row, dc * 8, D, vec);
-                }
-                *reinterpret_cast<u32x4*>(&sK[kr * KP + dc * 8]) = val;
-            }
-        }
-        // ---- stage V rows transposed: sV[d][key], 4 keys x 8 d per step
-        {
-            constexpr int CH = DP / 8;
-            for (int idx = threadIdx.x; idx < (BN / 4) * CH; idx += NT) {
-                const int kg = idx / CH, dc = idx % CH;
-                u32x4 rows4[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int n = n0 + kg * 4 + j;
-                    rows4[j] = u32x4{0u, 0u, 0u, 0u};
-                    if (n < ke) {
-                        const uint16_t* row = kv_row(p, p.v, p.v_s0, p.v_s1, p.v_s2, bt_row, it.k0, n, hk);
-                        rows4[j] = load8(row, dc * 8, D, vec);
-                    }
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    // d = dc*8 + 2w (low halves) and 2w+1 (high halves)
-                    const unsigned a0 = rows4[0][w], a1 = rows4[1][w], a2 = rows4[2][w], a3 = rows4[3][w];
-                    u32x2 even = u32x2{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                    u32x2 odd = u32x2{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-                    *reinterpret_cast<u32x2*>(&sV[(dc * 8 + 2 * w) * VP + kg * 4]) = even;
-                    *reinterpret_cast<u32x2*>(&sV[(dc * 8 + 2 * w + 1) * VP + kg * 4]) = odd;
-                }
-            }
-        }
-        __syncthreads();
+    // copy i of this thread covers tile row (wave*NI + i)*RPI + lane/CH and
+    // chunk position lane%CH (computed inside issue())
+    const int nchv = (D + 7) / 8;  // chunks that hold real columns
 
-        // ---- S^T = K Q^T for this wave's rows, one accumulator set per 32-key unit
-        constexpr int SPU = MR / 2;  // score values per lane per 32-key unit
-        float sc[NU][SPU];
+    const int kb_al = (kb / BN) * BN;
+    const int seg_keys = paged ? max(BN, ((kPageCap - 1) * P / BN) * BN) : INT_MAX;
+
+    for (int seg0 = kb_al; seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
+        const int seg1 = (seg_keys == INT_MAX) ? ke : min(ke, seg0 + seg_keys);
+        int pg_first = 0;
+        if (paged) {
+            __syncthreads();  // previous segment's users of s_pages and tiles are done
+            pg_first = seg0 / P;
+            const int npg = (seg1 - 1) / P - pg_first + 1;
+            for (int i = threadIdx.x; i < npg; i += NT) s_pages[i] = bt_row[pg_first + i];
+            __syncthreads();
+        }
+        const int ntiles = (seg1 - seg0 + BN - 1) / BN;
+
+        // issue the copies of tile t of this segment into stage t % NS
+        auto issue = [&](int t) {
+            const int ts = seg0 + t * BN;
+            unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
+            unsigned char* vbuf = kbuf + TILEB;
+            int pg0 = 0, pg1 = 0, base0 = 0;
+            if (paged) {
+                const int p0 = ts / P;
+                const int p1 = min(p0 + 1, (ke - 1) / P);
+                pg0 = s_pages[p0 - pg_first];
+                pg1 = s_pages[p1 - pg_first];
+                base0 = p0 * P;
+            }
+            const int ln = opaque_lane();
+            const int lrow = ln / CH;
+            const int lpos = ln % CH;
+            if (vec) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            if constexpr (MR == 32) {
-                // A row rho holds key u*32 + kappa(rho), kappa swaps bits 2 and 3
-                const int rho = rloc;
-                const int key = u * 32 + ((rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1));
-                const uint16_t* krow = &sK[key * KP + kgrp * 8];
-                acc_t s = {};
-#pragma unroll
-                for (int st = 0; st < NKS; ++st) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(krow + st * 16);
-                    s = M::mma(a, qreg[st], s);
+                for (int i = 0; i < NI; ++i) {
+                    const int rr = (wave * NI + i) * RPI + lrow;
+                    const int n = min(max(ts + rr, kb), ke - 1);
+                    int64_t offk, offv;
+                    if (paged) {
+                        const int off = n - base0;
+                        const int blk = off < P ? pg0 : pg1;
+                        const int slot = off < P ? off : off - P;
+                        offk = (int64_t)blk * p.k_s0 + (int64_t)slot * p.k_s1 + (int64_t)hk * p.k_s2;
+                        offv = (int64_t)blk * p.v_s0 + (int64_t)slot * p.v_s1 + (int64_t)hk * p.v_s2;
+                    } else {
+                        offk = (int64_t)(it.k0 + n) * p.k_s0 + (int64_t)hk * p.k_s1;
+                        offv = (int64_t)(it.k0 + n) * p.v_s0 + (int64_t)hk * p.v_s1;
+                    }
+                    int ck = lpos ^ (rr & SWK);
+                    int cv = lpos ^ ((2 * rr) & SWV);
+                    ck = ck < nchv ? ck : 0;
+                    cv = cv < nchv ? cv : 0;
+                    unsigned char* dst = smem + (t % NS) * 2 * TILEB + (wave * NI + i) * 1024;
+                    copy16_to_lds(p.k + offk + ck * 8, dst);
+                    copy16_to_lds(p.v + offv + cv * 8, dst + TILEB);
                 }
-#pragma unroll
-                for (int v = 0; v < 16; ++v) sc[u][v] = s[v];
             } else {
+                // unaligned or odd head dim: element-wise loads, zero fill, plain LDS stores
+#pragma unroll 1
+                for (int i = 0; i < NI; ++i) {
+                    const int rr = (wave * NI + i) * RPI + lrow;
+                    const int n = ts + rr;
+                    const bool ok = n >= kb && n < ke;
+                    const int nc = min(max(n, kb), ke - 1);
+                    const uint16_t *rowk, *rowv;
+                    if (paged) {
+                        const int off = nc - base0;
+                        const int blk = off < P ? pg0 : pg1;
+                        const int slot = off < P ? off : off - P;
+                        rowk = p.k + (int64_t)blk * p.k_s0 + (int64_t)slot * p.k_s1 + (int64_t)hk * p.k_s2;
+                        rowv = p.v + (int64_t)blk * p.v_s0 + (int64_t)slot * p.v_s1 + (int64_t)hk * p.v_s2;
+                    } else {
+                        rowk = p.k + (int64_t)(it.k0 + nc) * p.k_s0 + (int64_t)hk * p.k_s1;
+                        rowv = p.v + (int64_t)(it.k0 + nc) * p.v_s0 + (int64_t)hk * p.v_s1;
+                    }
+                    const int ck = lpos ^ (rr & SWK);
+                    const int cv = lpos ^ ((2 * rr) & SWV);
+                    const u32x4 zk = u32x4{0u, 0u, 0u, 0u};
+                    const u32x4 valk = ok ? load8(rowk, ck * 8, D, false) : zk;
+                    const u32x4 valv = ok ? load8(rowv, cv * 8, D, false) : zk;
+                    *reinterpret_cast<u32x4*>(kbuf + rr * ROWB + lpos * 16) = valk;
+                    *reinterpret_cast<u32x4*>(vbuf + rr * ROWB + lpos * 16) = valv;
+                }
+            }
+        };
+
 #pragma unroll
-                for (int sb = 0; sb < 2; ++sb) {
-                    const int rho = rloc;
-                    const int key = u * 32 + (rho >> 2) * 8 + sb * 4 + (rho & 3);
-                    const uint16_t* krow = &sK[key * KP + kgrp * 8];
+        for (int t = 0; t < NS - 1; ++t)
+            if (t < ntiles) issue(t);
+
+        for (int t = 0; t < ntiles; ++t) {
+            if (t + NS - 2 < ntiles) wait_vmcnt<(NS - 2) * 2 * NI>();
+            else wait_vmcnt<0>();
+            __syncthreads();  // tile t is in LDS for every wave; stage (t-1)%NS is free
+            if (t + NS - 1 < ntiles) issue(t + NS - 1);
+
+            const int n0 = seg0 + t * BN;
+            const unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
+            const unsigned char* vbuf = kbuf + TILEB;
+
+            // ---- S^T = K Q^T for this wave's rows, one accumulator set per 32-key unit
+            constexpr int SPU = MR / 2;  // score values per lane per 32-key unit
+            float sc[NU][SPU];
+#pragma unroll
+            for (int u = 0; u < NU; ++u) {
+                if constexpr (MR == 32) {
+                    // A row rho holds key u*32 + kappa(rho); kappa swaps bits 2 and 3.
+                    // Chunk st*2 + kgrp sits at position (st*2 + kgrp) ^ swz: the byte
+                    // offset is base ^ (st << 5) with base for st = 0.
+                    const int ln = opaque_lane();
+                    const int rl = ln & 31;
+                    const int kr = u * 32 + ((rl & ~12) | ((rl & 4) << 1) | ((rl & 8) >> 1));
+                    const int base = kr * ROWB + (((ln >> 5) ^ (kr & SWK)) << 4);
                     acc_t s = {};
 #pragma unroll
                     for (int st = 0; st < NKS; ++st) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + st * 32);
+                        const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + (base ^ (st << 5)));
                         s = M::mma(a, qreg[st], s);
                     }
 #pragma unroll
-                    for (int v = 0; v < 4; ++v) sc[u][sb * 4 + v] = s[v];
-                }
-            }
-        }
-
-        // ---- scale, mask, running max
-        const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
-        float mx = kNegInf;
+                    for (int v = 0; v < 16; ++v) sc[u][v] = s[v];
+                } else {
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+                    for (int sb = 0; sb < 2; ++sb) {
+                        // chunk st*4 + kgrp at position (st*4 + kgrp) ^ swz = base ^ (st << 6)
+                        const int ln = opaque_lane();
+                        const int rl = ln & 15;
+                        const int kr = u * 32 + (rl >> 2) * 8 + sb * 4 + (rl & 3);
+                        const int base = kr * ROWB + (((ln >> 4) ^ (kr & SWK)) << 4);
+                        acc_t s = {};
 #pragma unroll
-            for (int e = 0; e < SPU; ++e) {
-                float t = sc[u][e] * c2;
-                if (need_mask) {
-                    // key held by value e of unit u in this lane
-                    int key;
-                    if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
-                    else key = u * 32 + kgrp * 8 + e;
-                    const int n = n0 + key;
-                    if (n < lo || n >= hi) t = kNegInf;
-                }
-                sc[u][e] = t;
-                mx = fmaxf(mx, t);
-            }
-        if constexpr (MR == 32) {
-            mx = wave_max_xor(mx, 32);
-        } else {
-            mx = wave_max_xor(mx, 16);
-            mx = wave_max_xor(mx, 32);
-        }
-        const float m_new = fmaxf(m_run, mx);
-        const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-        float rs = 0.f;
-        unsigned int pk[NU][SPU / 2];
+                        for (int st = 0; st < NKS; ++st) {
+                            const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + (base ^ (st << 6)));
+                            s = M::mma(a, qreg[st], s);
+                        }
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
-#pragma unroll
-            for (int e = 0; e < SPU; e += 2) {
-                const float p0 = __builtin_amdgcn_exp2f(sc[u][e] - m_use);
-                const float p1 = __builtin_amdgcn_exp2f(sc[u][e + 1] - m_use);
-                rs += p0 + p1;
-                pk[u][e / 2] = pack_bf16x2(p0, p1);
-            }
-        if constexpr (MR == 32) {
-            rs += __shfl_xor(rs, 32, 64);
-        } else {
-            rs += __shfl_xor(rs, 16, 64);
-            rs += __shfl_xor(rs, 32, 64);
-        }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-            for (int v = 0; v < M::NACC; ++v) o[db][v] *= alpha;
-
-        // ---- O^T += V^T P^T
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            if constexpr (MR == 32) {
-#pragma unroll
-                for (int ts = 0; ts < 2; ++ts) {
-                    const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
-                                          pk[u][ts * 4 + 3]};
-                    const int kcol = u * 32 + ts * 16 + kgrp * 8;
-#pragma unroll
-                    for (int db = 0; db < NDB; ++db) {
-                        const u32x4 a =
-                            *reinterpret_cast<const u32x4*>(&sV[(db * 32 + rloc) * VP + kcol]);
-                        o[db] = M::mma(a, b, o[db]);
+                        for (int v = 0; v < 4; ++v) sc[u][sb * 4 + v] = s[v];
                     }
                 }
-            } else {
-                const u32x4 b = u32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
-                const int kcol = u * 32 + kgrp * 8;
+            }
+
+            // ---- scale, mask, running max
+            const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
+            float mx = kNegInf;
 #pragma unroll
-                for (int db = 0; db < NDB; ++db) {
-                    const u32x4 a = *reinterpret_cast<const u32x4*>(&sV[(db * 16 + rloc) * VP + kcol]);
-                    o[db] = M::mma(a, b, o[db]);
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int e = 0; e < SPU; ++e) {
+                    float tv = sc[u][e] * c2;
+                    if (need_mask) {
+                        int key;
+                        if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
+                        else key = u * 32 + kgrp * 8 + e;
+                        const int n = n0 + key;
+                        if (n < lo || n >= hi) tv = kNegInf;
+                    }
+                    sc[u][e] = tv;
+                    mx = fmaxf(mx, tv);
+                }
+            if constexpr (MR == 32) {
+                mx = wave_max_xor(mx, 32);
+            } else {
+                mx = wave_max_xor(mx, 16);
+                mx = wave_max_xor(mx, 32);
+            }
+            const float m_new = fmaxf(m_run, mx);
+            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            float rs = 0.f;
+            unsigned int pk[NU][SPU / 2];
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int e = 0; e < SPU; e += 2) {
+                    const float p0 = __builtin_amdgcn_exp2f(sc[u][e] - m_use);
+                    const float p1 = __builtin_amdgcn_exp2f(sc[u][e + 1] - m_use);
+                    rs += p0 + p1;
+                    pk[u][e / 2] = pack_bf16x2(p0, p1);
+                }
+            if constexpr (MR == 32) {
+                rs += __shfl_xor(rs, 32, 64);
+            } else {
+                rs += __shfl_xor(rs, 16, 64);
+                rs += __shfl_xor(rs, 32, 64);
+            }
+            l_run = l_run * alpha + rs;
+            m_run = m_new;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int v = 0; v < M::NACC; ++v) o[db][v] *= alpha;
+
+            // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  For d-block
+            // db the chunk index is db*(MR/8) + low bits, so the byte offset within
+            // the row is base ^ (db * MR * 2) with base computed for db = 0.
+            {
+                const int ln = opaque_lane();
+                const int g16 = ln >> 4;
+                const int a16 = ln & 15;
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    if constexpr (MR == 32) {
+#pragma unroll
+                        for (int ts = 0; ts < 2; ++ts) {
+                            const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
+                                                  pk[u][ts * 4 + 3]};
+                            const int r0 = u * 32 + ts * 16 + (g16 >> 1) * 8 + (a16 >> 2);
+                            const int r1 = r0 + 4;
+                            const int c0 = (g16 & 1) * 2 + ((a16 >> 1) & 1);
+                            const int b0 = r0 * ROWB + ((c0 ^ ((2 * r0) & SWV)) << 4) + (a16 & 1) * 8;
+                            const int b1 = r1 * ROWB + ((c0 ^ ((2 * r1) & SWV)) << 4) + (a16 & 1) * 8;
+#pragma unroll
+                            for (int db = 0; db < NDB; ++db) {
+                                const u32x2 lo2 = lds_read_tr16(vbuf + (b0 ^ (db << 6)));
+                                const u32x2 hi2 = lds_read_tr16(vbuf + (b1 ^ (db << 6)));
+                                const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+                                o[db] = M::mma(a, b, o[db]);
+                            }
+                        }
+                    } else {
+                        const u32x4 b = u32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
+                        const int r0 = u * 32 + g16 * 8 + (a16 >> 2);
+                        const int r1 = r0 + 4;
+                        const int c0 = (a16 >> 1) & 1;
+                        const int b0 = r0 * ROWB + ((c0 ^ ((2 * r0) & SWV)) << 4) + (a16 & 1) * 8;
+                        const int b1 = r1 * ROWB + ((c0 ^ ((2 * r1) & SWV)) << 4) + (a16 & 1) * 8;
+#pragma unroll
+                        for (int db = 0; db < NDB; ++db) {
+                            const u32x2 lo2 = lds_read_tr16(vbuf + (b0 ^ (db << 5)));
+                            const u32x2 hi2 = lds_read_tr16(vbuf + (b1 ^ (db << 5)));
+                            const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+                            o[db] = M::mma(a, b, o[db]);
+                        }
+                    }
                 }
             }
         }
@@ -532,26 +651,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
 
 hipError_t g_last = hipSuccess;
 
-template <int DP, int MR, int WR, int BN>
+template <int DP, int MR, int WR, int BN, int NS>
 hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
     dim3 grid((unsigned)plan.grid_x, (unsigned)p.Hk);
-    hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN>), grid, dim3(64 * WR), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
     return hipGetLastError();
 }
 
 template <int DP>
 hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
     if (plan.kind == KIND_PREFILL) {
-        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64>(plan, p, s);
-        else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32>(plan, p, s);
-        else return launch_attn<DP, 16, 4, 32>(plan, p, s);
+        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64, 2>(plan, p, s);
+        else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32, 2>(plan, p, s);
+        else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
     }
-    // decode: 16 rows per wave, split keys over workgroups
+    // decode: 16 rows per wave, keys split over workgroups
     if (plan.wr == 1) {
-        if constexpr (DP <= 256) return launch_attn<DP, 16, 1, 32>(plan, p, s);
-        else return launch_attn<DP, 16, 1, 32>(plan, p, s);
+        if constexpr (DP <= 128) return launch_attn<DP, 16, 1, 32, 3>(plan, p, s);
+        else return launch_attn<DP, 16, 1, 32, 2>(plan, p, s);
     }
-    return launch_attn<DP, 16, 4, 32>(plan, p, s);
+    if constexpr (DP <= 256) return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
+    else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
 }
 
 template <int DP>
