@@ -220,7 +220,7 @@ __device__ __forceinline__ int opaque_lane() {
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
 template <int DP, int MR, int WR, int BN, int NS>
-__global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * WR, (DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR> M;
     typedef typename M::acc_t acc_t;
     constexpr int NT = 64 * WR;
@@ -291,13 +291,22 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
         w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
     }
 
-    // Q^T operand: lane holds q[row][s*KSTEP + kgrp*8 .. +8) for every k-step s
+    // Q^T operand: lane holds q[row][s*KSTEP + kgrp*8 .. +8) for every k-step s.
+    // The softmax below needs a positive scale: a negative scale is applied as
+    // an exact sign flip of q, a zero scale as q = 0 with scale 1 (uniform weights).
+    float c2 = p.scale_log2;
+    unsigned int qflip = 0u;
+    bool qzero = false;
+    if (c2 < 0.f) { qflip = 0x80008000u; c2 = -c2; }
+    if (c2 == 0.f) { qzero = true; c2 = 1.f; }
     u32x4 qreg[NKS];
     {
         const uint16_t* qrow = p.q + (int64_t)(it.q0 + qi) * p.q_s0 + (int64_t)h * p.q_s1;
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
-            qreg[s] = row_ok ? load8(qrow, s * M::KSTEP + kgrp * 8, D, vec) : u32x4{0u, 0u, 0u, 0u};
+        for (int s = 0; s < NKS; ++s) {
+            u32x4 x = (row_ok && !qzero) ? load8(qrow, s * M::KSTEP + kgrp * 8, D, vec) : u32x4{0u, 0u, 0u, 0u};
+            qreg[s] = x ^ u32x4{qflip, qflip, qflip, qflip};
+        }
     }
 
     acc_t o[NDB];
@@ -305,8 +314,10 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int v = 0; v < M::NACC; ++v) o[db][v] = 0.f;
+    // running max (log2 domain) and sum of the rows; m_run is a reference
+    // value that only moves when the tile max exceeds it by more than 8, so the
+    // O rescale is rare and probabilities stay <= 2^8
     float m_run = kNegInf, l_run = 0.f;
-    const float c2 = p.scale_log2;
 
     // copy i of this thread covers tile row (wave*NI + i)*RPI + lane/CH and
     // chunk position lane%CH (computed inside issue())
@@ -452,56 +463,69 @@ __global__ __launch_bounds__(64 * WR) void attn_fwd_kernel(const FwdParams p) {
                 }
             }
 
-            // ---- scale, mask, running max
+            // ---- mask, running max (raw scores; c2 > 0 so the scaled max is c2 * max)
             const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
             float mx = kNegInf;
+            if (need_mask) {
 #pragma unroll
-            for (int u = 0; u < NU; ++u)
+                for (int u = 0; u < NU; ++u)
 #pragma unroll
-                for (int e = 0; e < SPU; ++e) {
-                    float tv = sc[u][e] * c2;
-                    if (need_mask) {
+                    for (int e = 0; e < SPU; ++e) {
                         int key;
                         if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
                         else key = u * 32 + kgrp * 8 + e;
                         const int n = n0 + key;
-                        if (n < lo || n >= hi) tv = kNegInf;
+                        if (n < lo || n >= hi) sc[u][e] = kNegInf;
                     }
-                    sc[u][e] = tv;
-                    mx = fmaxf(mx, tv);
-                }
+            }
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int e = 0; e < SPU; ++e) mx = fmaxf(mx, sc[u][e]);
             if constexpr (MR == 32) {
                 mx = wave_max_xor(mx, 32);
             } else {
                 mx = wave_max_xor(mx, 16);
                 mx = wave_max_xor(mx, 32);
             }
-            const float m_new = fmaxf(m_run, mx);
-            const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            float rs = 0.f;
+            mx *= c2;
+            const bool grow = mx > m_run + 8.f;
+            if (__ballot(grow)) {
+                // rows that do not grow keep alpha = 1 (their m_run may still be -inf)
+                const float m_new = grow ? mx : m_run;
+                const float alpha = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.f;
+                l_run *= alpha;
+                m_run = m_new;
+#pragma unroll
+                for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                    for (int v = 0; v < M::NACC; ++v) o[db][v] *= alpha;
+            }
+            const float nm = (m_run == kNegInf) ? 0.f : -m_run;
+            float rs0 = 0.f, rs1 = 0.f;
             unsigned int pk[NU][SPU / 2];
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int e = 0; e < SPU; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(sc[u][e] - m_use);
-                    const float p1 = __builtin_amdgcn_exp2f(sc[u][e + 1] - m_use);
-                    rs += p0 + p1;
-                    pk[u][e / 2] = pack_bf16x2(p0, p1);
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e], c2, nm));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e + 1], c2, nm));
+                    const unsigned int pp = pack_bf16x2(p0, p1);
+                    pk[u][e / 2] = pp;
+                    // row sum of the bf16-rounded probabilities that feed the PV product
+                    if ((e / 2) & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, rs1, false);
+                    else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, rs0, false);
                 }
+            float rs = rs0 + rs1;
             if constexpr (MR == 32) {
                 rs += __shfl_xor(rs, 32, 64);
             } else {
                 rs += __shfl_xor(rs, 16, 64);
                 rs += __shfl_xor(rs, 32, 64);
             }
-            l_run = l_run * alpha + rs;
-            m_run = m_new;
-#pragma unroll
-            for (int db = 0; db < NDB; ++db)
-#pragma unroll
-                for (int v = 0; v < M::NACC; ++v) o[db][v] *= alpha;
+            l_run += rs;
 
             // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  For d-block
             // db the chunk index is db*(MR/8) + low bits, so the byte offset within
