@@ -272,10 +272,16 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     p.chunk = plan.chunk;
     p.max_chunks = plan.max_chunks;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
-    if (plan.ws_bytes) {
-        const size_t n_o = (size_t)plan.max_chunks * (size_t)total_q * (size_t)p.H * (size_t)plan.dp;
-        p.part_o = static_cast<float*>(workspace);
-        p.part_lse = p.part_o + n_o;
+    {
+        unsigned char* ws = static_cast<unsigned char*>(workspace);
+        if (plan.max_chunks > 1) {
+            const size_t n_o = (size_t)plan.max_chunks * (size_t)total_q * (size_t)p.H * (size_t)plan.dp;
+            p.part_o = reinterpret_cast<float*>(ws);
+            p.part_lse = p.part_o + n_o;
+        }
+        p.items = reinterpret_cast<int4*>(ws + plan.off_items);
+        p.item_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
+        p.seq_off = reinterpret_cast<int32_t*>(ws + plan.off_seq);
     }
     // 16-byte vector access is legal when every row start is 16-byte aligned
     bool vec = (p.D % 8 == 0);

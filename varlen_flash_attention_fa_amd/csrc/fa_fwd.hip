@@ -112,55 +112,9 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
 }
 
 struct Item {
-    int b, rt, c, nc;
+    int b, rt, c, nc, gid;
     int q0, Lq, k0, Lk;
 };
-
-// Map a flat work-item index to (sequence, row tile, chunk).  Items are
-// numbered sequence by sequence; sequence b owns ceil(Lq*G/R) row tiles times
-// nc(b) chunks.  Every wave of the workgroup runs this redundantly (no LDS).
-__device__ bool locate(const FwdParams& p, int item, int R, bool split, Item* out) {
-    const int lane = threadIdx.x & 63;
-    int remaining = item;
-    for (int base = 0; base < p.batch; base += 64) {
-        const int b = base + lane;
-        int q0 = 0, lq = 0, k0 = 0, lk = 0, cnt = 0, nc = 1;
-        if (b < p.batch) {
-            q0 = p.cu_q[b];
-            lq = p.cu_q[b + 1] - q0;
-            k0 = p.cu_k[b];
-            lk = p.cu_k[b + 1] - k0;
-            nc = split ? min(p.max_chunks, max(1, ceil_div(lk, p.chunk))) : 1;
-            cnt = ceil_div(lq * p.G, R) * nc;
-        }
-        int incl = cnt;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            int t = __shfl_up(incl, off, 64);
-            if (lane >= off) incl += t;
-        }
-        const int total = __shfl(incl, 63, 64);
-        if (remaining < total) {
-            const unsigned long long hit = __ballot(incl > remaining);
-            const int src = __ffsll((long long)hit) - 1;
-            Item it;
-            it.b = __shfl(b, src, 64);
-            it.q0 = __shfl(q0, src, 64);
-            it.Lq = __shfl(lq, src, 64);
-            it.k0 = __shfl(k0, src, 64);
-            it.Lk = __shfl(lk, src, 64);
-            it.nc = __shfl(nc, src, 64);
-            const int before = __shfl(incl - cnt, src, 64);
-            const int local = remaining - before;
-            it.rt = local / it.nc;
-            it.c = local % it.nc;
-            *out = it;
-            return true;
-        }
-        remaining -= total;
-    }
-    return false;
-}
 
 // Key ranges are [lo, hi) in sequence-local key positions.
 struct Range {
@@ -211,6 +165,115 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }  // block-table entries staged in LDS per segment
 
+// ---------------------------------------------------------------- planner
+//
+// One workgroup turns cu_seqlens into the work list of the main kernel:
+// sequence b owns ceil(Lq_b*G/R) row tiles times nc_b key chunks.  Items are
+// written in decreasing order of estimated cost (rows x visible keys, in
+// half-octave buckets); the main kernel's workgroup x handles item x, and
+// workgroups are dispatched in index order, so the longest items start first
+// and the short ones fill the tail.
+constexpr int kPlanThreads = 1024;
+constexpr int kCostBuckets = 128;
+constexpr int kLdsSeqs = 4096;
+
+__device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk) {
+    return p.max_chunks > 1 ? min(p.max_chunks, max(1, ceil_div(lk, p.chunk))) : 1;
+}
+
+__device__ __forceinline__ int cost_bucket(int64_t cost) {
+    if (cost <= 0) return 0;
+    const int lg = 63 - __builtin_clzll((unsigned long long)cost);
+    const int half = lg >= 1 ? (int)((cost >> (lg - 1)) & 1) : 0;
+    return min(kCostBuckets - 1, 1 + 2 * lg + half);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
+    __shared__ int s_off_lds[kLdsSeqs + 1];
+    __shared__ int s_scan[kPlanThreads];
+    __shared__ int s_hist[kCostBuckets];
+    const int tid = threadIdx.x;
+    int* off = p.batch <= kLdsSeqs ? s_off_lds : p.seq_off;
+    const bool split = p.max_chunks > 1;
+    const int R = p.rows;
+
+    for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_hist[i] = 0;
+
+    // items per sequence -> exclusive offsets off[0..batch]
+    int carry = 0;
+    for (int base = 0; base < p.batch; base += kPlanThreads) {
+        const int b = base + tid;
+        int cnt = 0;
+        if (b < p.batch) {
+            const int lq = p.cu_q[b + 1] - p.cu_q[b];
+            const int lk = p.cu_k[b + 1] - p.cu_k[b];
+            cnt = ceil_div(lq * p.G, R) * seq_chunks(p, lk);
+        }
+        s_scan[tid] = cnt;
+        __syncthreads();
+        for (int o = 1; o < kPlanThreads; o <<= 1) {
+            const int x = tid >= o ? s_scan[tid - o] : 0;
+            __syncthreads();
+            s_scan[tid] += x;
+            __syncthreads();
+        }
+        if (b < p.batch) off[b] = carry + s_scan[tid] - cnt;
+        carry += s_scan[kPlanThreads - 1];
+        __syncthreads();
+    }
+    const int total = min(carry, p.items_bound);
+    if (tid == 0) {
+        off[p.batch] = carry;
+        *p.item_count = total;
+    }
+    __syncthreads();
+
+    // decode item i -> (b, rt, c, nc, cost bucket); the first pass counts
+    // buckets, the second places each item at its bucket's next slot
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int i = tid; i < total; i += kPlanThreads) {
+            int lo = 0, hi = p.batch;  // last b with off[b] <= i
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid;
+            }
+            const int b = lo;
+            const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
+            const int lk = p.cu_k[b + 1] - p.cu_k[b];
+            const int nc = seq_chunks(p, lk);
+            const int local = i - off[b];
+            const int rt = local / nc, c = local % nc;
+            const int nrows = lq * p.G;
+            const int r0 = rt * R, r1 = min(nrows, r0 + R) - 1;
+            const Range a = row_range(p, r0 / p.G, lq, lk);
+            const Range z = row_range(p, r1 / p.G, lq, lk);
+            int kb = a.lo, ke = z.hi;
+            if (split) {
+                kb = max(kb, c * p.chunk);
+                ke = min(ke, (c + 1) * p.chunk);
+            }
+            const int64_t cost = (int64_t)max(0, ke - kb) * (r1 - r0 + 1) + (r1 - r0 + 1);
+            const int bucket = cost_bucket(cost);
+            if (pass == 0) {
+                atomicAdd(&s_hist[bucket], 1);
+            } else {
+                const int pos = atomicAdd(&s_hist[bucket], 1);
+                p.items[pos] = make_int4(b, rt, c | (nc << 16), 0);
+            }
+        }
+        __syncthreads();
+        if (pass == 0 && tid == 0) {  // bucket starts, most expensive first
+            int run = 0;
+            for (int k = kCostBuckets - 1; k >= 0; --k) {
+                const int cnt = s_hist[k];
+                s_hist[k] = run;
+                run += cnt;
+            }
+        }
+        __syncthreads();
+    }
+}
+
 // Main attention kernel.
 //   DP: head dim padded to 64/128/256/512      MR: rows per wave (MFMA 32x32x16 or 16x16x32)
 //   WR: waves per workgroup (they share K/V)    BN: keys per tile     NS: LDS pipeline stages
@@ -220,7 +283,7 @@ __device__ __forceinline__ int opaque_lane() {
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
 template <int DP, int MR, int WR, int BN, int NS>
-__global__ __launch_bounds__(64 * WR, (DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
+__global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR> M;
     typedef typename M::acc_t acc_t;
     constexpr int NT = 64 * WR;
@@ -249,11 +312,22 @@ __global__ __launch_bounds__(64 * WR, (DP <= 128 ? 2 : 1)) void attn_fwd_kernel(
     const bool paged = p.bt != nullptr;
     const int P = p.page;
 
+    // one workgroup per work item, in the planner's order (largest first);
+    // workgroups past the end of the list exit
+    const int item_idx = blockIdx.x;
+    if (item_idx >= *p.item_count) return;
     Item it;
-    if (!locate(p, blockIdx.x, R, split, &it)) return;
-    if (!split) {  // heaviest (last) row tiles of a causal sequence first
-        const int nrt = ceil_div(it.Lq * p.G, R);
-        it.rt = nrt - 1 - it.rt;
+    {
+        const int4 d = p.items[item_idx];
+        it.b = d.x;
+        it.rt = d.y;
+        it.c = d.z & 0xffff;
+        it.nc = d.z >> 16;
+        it.gid = d.w;
+        it.q0 = p.cu_q[it.b];
+        it.Lq = p.cu_q[it.b + 1] - it.q0;
+        it.k0 = p.cu_k[it.b];
+        it.Lk = p.cu_k[it.b + 1] - it.k0;
     }
     const int Lq = it.Lq, Lk = it.Lk;
     const int nrows = Lq * p.G;
@@ -575,12 +649,27 @@ __global__ __launch_bounds__(64 * WR, (DP <= 128 ? 2 : 1)) void attn_fwd_kernel(
     }
 
     // ---- epilogue
-    if (!row_ok) return;
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse2 = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : kNegInf;
-    const int t = it.q0 + qi;
+    const int tq = it.q0 + qi;
     if (split && it.nc > 1) {
-        float* po = p.part_o + (((int64_t)it.c * p.total_q + t) * p.H + h) * DP;
+        if (row_ok) {
+            float* po = p.part_o + (((int64_t)it.c * p.total_q + tq) * p.H + h) * DP;
+#pragma unroll
+            for (int db = 0; db < NDB; ++db)
+#pragma unroll
+                for (int v4 = 0; v4 < M::NACC; v4 += 4) {
+                    int d;
+                    if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
+                    else d = db * 16 + kgrp * 4;
+                    f32x4 val = {o[db][v4] * inv, o[db][v4 + 1] * inv, o[db][v4 + 2] * inv,
+                                 o[db][v4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(po + d) = val;
+                }
+            if (kgrp == 0) p.part_lse[((int64_t)it.c * p.total_q + tq) * p.H + h] = lse2;
+        }
+    } else if (row_ok) {
+        uint16_t* orow = p.out + (int64_t)tq * p.o_s0 + (int64_t)h * p.o_s1;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -588,34 +677,20 @@ __global__ __launch_bounds__(64 * WR, (DP <= 128 ? 2 : 1)) void attn_fwd_kernel(
                 int d;
                 if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
                 else d = db * 16 + kgrp * 4;
-                f32x4 val = {o[db][v4] * inv, o[db][v4 + 1] * inv, o[db][v4 + 2] * inv,
-                             o[db][v4 + 3] * inv};
-                *reinterpret_cast<f32x4*>(po + d) = val;
+                if (d >= D) continue;
+                const float x0 = o[db][v4] * inv, x1 = o[db][v4 + 1] * inv;
+                const float x2 = o[db][v4 + 2] * inv, x3 = o[db][v4 + 3] * inv;
+                if (vec) {
+                    *reinterpret_cast<u32x2*>(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                } else {
+                    const float xs[4] = {x0, x1, x2, x3};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        if (d + j < D) orow[d + j] = to_bf16(xs[j]);
+                }
             }
-        if (kgrp == 0) p.part_lse[((int64_t)it.c * p.total_q + t) * p.H + h] = lse2;
-        return;
+        if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.total_q + tq] = lse2 * 0.6931471805599453f;
     }
-    uint16_t* orow = p.out + (int64_t)t * p.o_s0 + (int64_t)h * p.o_s1;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-        for (int v4 = 0; v4 < M::NACC; v4 += 4) {
-            int d;
-            if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
-            else d = db * 16 + kgrp * 4;
-            if (d >= D) continue;
-            const float x0 = o[db][v4] * inv, x1 = o[db][v4 + 1] * inv;
-            const float x2 = o[db][v4 + 2] * inv, x3 = o[db][v4 + 3] * inv;
-            if (vec) {
-                *reinterpret_cast<u32x2*>(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
-            } else {
-                const float xs[4] = {x0, x1, x2, x3};
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    if (d + j < D) orow[d + j] = to_bf16(xs[j]);
-            }
-        }
-    if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.total_q + t] = lse2 * 0.6931471805599453f;
 }
 
 // Merge split partials: one wave per (token, head).
@@ -677,8 +752,15 @@ hipError_t g_last = hipSuccess;
 
 template <int DP, int MR, int WR, int BN, int NS>
 hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
-    dim3 grid((unsigned)plan.grid_x, (unsigned)p.Hk);
+    dim3 grid((unsigned)plan.items_bound, (unsigned)p.Hk);
     hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
+    return hipGetLastError();
+}
+
+template <int DP>
+hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
+    dim3 grid((unsigned)p.total_q, (unsigned)((p.H + 3) / 4));
+    hipLaunchKernelGGL((combine_kernel<DP>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -689,20 +771,12 @@ hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
         else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32, 2>(plan, p, s);
         else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
     }
-    // decode: 16 rows per wave, keys split over workgroups
+    // decode: 16 rows per wave, keys split over work items
     if (plan.wr == 1) {
         if constexpr (DP <= 128) return launch_attn<DP, 16, 1, 32, 3>(plan, p, s);
         else return launch_attn<DP, 16, 1, 32, 2>(plan, p, s);
     }
-    if constexpr (DP <= 256) return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
-    else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
-}
-
-template <int DP>
-hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
-    dim3 grid((unsigned)p.total_q, (unsigned)((p.H + 3) / 4));
-    hipLaunchKernelGGL((combine_kernel<DP>), grid, dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
 }
 
 int env_int(const char* name, int dflt) {
@@ -710,6 +784,8 @@ int env_int(const char* name, int dflt) {
     if (!s || !*s) return dflt;
     return std::atoi(s);
 }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -737,7 +813,7 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.mr = 16;
         P.wr = rows_avg <= 16 ? 1 : 4;
         P.bn = 32;
-        int chunk = P.dp <= 128 ? 256 : P.dp == 256 ? 512 : 1024;
+        int chunk = P.dp <= 128 ? 512 : 1024;
         chunk = env_int("FA_SPLIT_KEYS", chunk);
         if (chunk < P.bn) chunk = P.bn;
         chunk = (chunk + P.bn - 1) / P.bn * P.bn;
@@ -749,26 +825,43 @@ int make_plan(const Shapes& s, Plan* plan) {
     }
     P.rows = P.mr * P.wr;
     const int64_t tiles = (s.total_q * G + P.rows - 1) / P.rows + s.batch;
-    const int64_t gx = tiles * P.max_chunks;
-    if (gx >= INT32_MAX || s.Hk > 65535) return FA_ERR_ARGUMENT;
-    P.grid_x = gx;
-    P.ws_bytes = P.max_chunks > 1
-                     ? (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * (size_t)(P.dp + 1) * 4u
-                     : 0;
+    const int64_t items = tiles * P.max_chunks;
+    if (items >= INT32_MAX / 2 || s.Hk > 65535) return FA_ERR_ARGUMENT;
+    P.items_bound = items;
+    // workspace: [split partials o][split partials lse][items][count][seq offsets]
+    size_t off = 0;
+    if (P.max_chunks > 1) {
+        off += (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * (size_t)P.dp * 4u;
+        off += (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * 4u;
+    }
+    off = align256(off);
+    P.off_items = off;
+    off = align256(off + (size_t)items * 16u);
+    P.off_count = off;
+    off = align256(off + 4u);
+    P.off_seq = off;
+    off = align256(off + (size_t)(s.batch + 1) * 4u);
+    P.ws_bytes = off;
     *plan = P;
     return 0;
 }
 
-int launch_fwd(const Plan& plan, const FwdParams& p, void* stream, void* ev_start, void* ev_stop) {
+int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);
+    FwdParams p = p_in;
+    p.rows = plan.rows;
+    p.items_bound = (int32_t)plan.items_bound;
     hipError_t e = hipSuccess;
-    if (ev_start) e = hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
-    if (e != hipSuccess) { g_last = e; return FA_ERR_HIP; }
-    switch (plan.dp) {
-        case 64: e = launch_dp<64>(plan, p, s); break;
-        case 128: e = launch_dp<128>(plan, p, s); break;
-        case 256: e = launch_dp<256>(plan, p, s); break;
-        default: e = launch_dp<512>(plan, p, s); break;
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
+    e = hipGetLastError();
+    if (e == hipSuccess && ev_start) e = hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
+    if (e == hipSuccess) {
+        switch (plan.dp) {
+            case 64: e = launch_dp<64>(plan, p, s); break;
+            case 128: e = launch_dp<128>(plan, p, s); break;
+            case 256: e = launch_dp<256>(plan, p, s); break;
+            default: e = launch_dp<512>(plan, p, s); break;
+        }
     }
     if (e == hipSuccess && ev_stop) e = hipEventRecord(static_cast<hipEvent_t>(ev_stop), s);
     if (e == hipSuccess && plan.max_chunks > 1) {

@@ -29,6 +29,11 @@ struct FwdParams {
     int32_t window_left, window_right;
     int32_t chunk;          // keys per split (split only if max_chunks > 1)
     int32_t max_chunks;
+    int32_t rows;           // rows per work item (MFMA rows per wave * waves)
+    int32_t items_bound;    // upper bound of the number of work items per K/V head
+    int4* items;            // work list written by the planner: {b, rt, c | nc<<16, 0}
+    int32_t* item_count;    // number of work items (per K/V head)
+    int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
     float scale_log2;       // softmax_scale * log2(e)
 };
@@ -44,7 +49,8 @@ struct Plan {
     int rows;       // rows per workgroup = mr * wr
     int chunk;      // keys per split
     int max_chunks; // upper bound of splits per sequence
-    int64_t grid_x; // workgroups along x (upper bound of work items)
+    int64_t items_bound;  // upper bound of work items per K/V head
+    size_t off_items, off_count, off_seq;  // workspace layout (bytes)
     size_t ws_bytes;
 };
 
