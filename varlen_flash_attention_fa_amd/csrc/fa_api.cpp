@@ -149,6 +149,7 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
             return fail(FA_ERR_CONTIGUOUS, "block_table last dimension must be contiguous");
         if (bt->shape[1] * (int64_t)page_block_size >= INT32_MAX)
             return fail(FA_ERR_ARGUMENT, "max_blocks * page_block_size must be below 2^31");
+        if (k->shape[0] >= INT32_MAX) return fail(FA_ERR_ARGUMENT, "num_blocks must be below 2^31");
     } else if (k->shape[0] >= INT32_MAX) {
         return fail(FA_ERR_ARGUMENT, "total_k must be below 2^31");
     }
@@ -262,6 +263,8 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
         p.v_s0 = v->stride[0]; p.v_s1 = v->stride[1]; p.v_s2 = 0;
     }
     p.batch = batch;
+    p.max_lk = (int32_t)(paged ? block_table->shape[1] * (int64_t)page_block_size : k->shape[0]);
+    p.num_blocks = (int32_t)(paged ? k->shape[0] : 0);
     p.H = (int32_t)q->shape[1];
     p.Hk = (int32_t)(paged ? k->shape[2] : k->shape[1]);
     p.G = p.H / p.Hk;

@@ -165,6 +165,32 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }  // block-table entries staged in LDS per segment
 
+// Sequence b's query rows [q0, q0+Lq) and key count Lk, clamped to the
+// tensors the call was given: cu_seqlens contents are not validated, and a bad
+// table must not make any kernel address outside q/out, k/v or the block table.
+struct SeqSpan {
+    int q0, Lq, k0, Lk;
+};
+
+__device__ __forceinline__ SeqSpan seq_span(const FwdParams& p, int b) {
+    SeqSpan s;
+    const int q0 = min(max(p.cu_q[b], 0), p.total_q);
+    const int q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    s.q0 = q0;
+    s.Lq = q1 - q0;
+    const int k0 = p.cu_k[b];
+    int lk = max(0, p.cu_k[b + 1] - k0);
+    if (p.bt) {
+        s.k0 = 0;
+        lk = p.num_blocks > 0 ? min(lk, p.max_lk) : 0;
+    } else {
+        s.k0 = min(max(k0, 0), p.max_lk);
+        lk = min(lk, p.max_lk - s.k0);
+    }
+    s.Lk = lk;
+    return s;
+}
+
 // ---------------------------------------------------------------- planner
 //
 // One workgroup turns cu_seqlens into the work list of the main kernel:
@@ -205,9 +231,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
         const int b = base + tid;
         int cnt = 0;
         if (b < p.batch) {
-            const int lq = p.cu_q[b + 1] - p.cu_q[b];
-            const int lk = p.cu_k[b + 1] - p.cu_k[b];
-            cnt = ceil_div(lq * p.G, R) * seq_chunks(p, lk);
+            const SeqSpan sp = seq_span(p, b);
+            cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk);
         }
         s_scan[tid] = cnt;
         __syncthreads();
@@ -238,8 +263,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 if (off[mid] <= i) lo = mid; else hi = mid;
             }
             const int b = lo;
-            const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
-            const int lk = p.cu_k[b + 1] - p.cu_k[b];
+            const SeqSpan sp = seq_span(p, b);
+            const int lq = sp.Lq, lk = sp.Lk;
             const int nc = seq_chunks(p, lk);
             const int local = i - off[b];
             const int rt = local / nc, c = local % nc;
@@ -258,7 +283,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 atomicAdd(&s_hist[bucket], 1);
             } else {
                 const int pos = atomicAdd(&s_hist[bucket], 1);
-                p.items[pos] = make_int4(b, rt, c | (nc << 16), 0);
+                p.items[2 * pos] = make_int4(b, rt, c | (nc << 16), 0);
+                p.items[2 * pos + 1] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             }
         }
         __syncthreads();
@@ -318,16 +344,17 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     if (item_idx >= *p.item_count) return;
     Item it;
     {
-        const int4 d = p.items[item_idx];
+        const int4 d = p.items[2 * item_idx];
+        const int4 e = p.items[2 * item_idx + 1];
         it.b = d.x;
         it.rt = d.y;
         it.c = d.z & 0xffff;
         it.nc = d.z >> 16;
         it.gid = d.w;
-        it.q0 = p.cu_q[it.b];
-        it.Lq = p.cu_q[it.b + 1] - it.q0;
-        it.k0 = p.cu_k[it.b];
-        it.Lk = p.cu_k[it.b + 1] - it.k0;
+        it.q0 = e.x;
+        it.Lq = e.y;
+        it.k0 = e.z;
+        it.Lk = e.w;
     }
     const int Lq = it.Lq, Lk = it.Lk;
     const int nrows = Lq * p.G;
@@ -400,14 +427,16 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     const int kb_al = (kb / BN) * BN;
     const int seg_keys = paged ? max(BN, ((kPageCap - 1) * P / BN) * BN) : INT_MAX;
 
-    for (int seg0 = kb_al; seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
+    // (an empty range, kb >= ke, runs no tile: its rows keep l = 0 and give 0)
+    for (int seg0 = kb_al; kb < ke && seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
         const int seg1 = (seg_keys == INT_MAX) ? ke : min(ke, seg0 + seg_keys);
         int pg_first = 0;
         if (paged) {
             __syncthreads();  // previous segment's users of s_pages and tiles are done
             pg_first = seg0 / P;
             const int npg = (seg1 - 1) / P - pg_first + 1;
-            for (int i = threadIdx.x; i < npg; i += NT) s_pages[i] = bt_row[pg_first + i];
+            for (int i = threadIdx.x; i < npg; i += NT)  // block ids clamped into the pool
+                s_pages[i] = min(max(bt_row[pg_first + i], 0), p.num_blocks - 1);
             __syncthreads();
         }
         const int ntiles = (seg1 - seg0 + BN - 1) / BN;
@@ -420,7 +449,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             int pg0 = 0, pg1 = 0, base0 = 0;
             if (paged) {
                 const int p0 = ts / P;
-                const int p1 = min(p0 + 1, (ke - 1) / P);
+                const int p1 = min(p0 + 1, (seg1 - 1) / P);  // only pages staged for this segment
                 pg0 = s_pages[p0 - pg_first];
                 pg1 = s_pages[p1 - pg_first];
                 base0 = p0 * P;
@@ -708,7 +737,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
         if (p.cu_q[mid] <= t) lo = mid; else hi = mid;
     }
     const int b = lo;
-    const int Lk = p.cu_k[b + 1] - p.cu_k[b];
+    const int Lk = seq_span(p, b).Lk;
     const int nc = min(p.max_chunks, max(1, ceil_div(Lk, p.chunk)));
     if (nc <= 1) return;
     const float* pl = p.part_lse + (int64_t)t * p.H + h;
@@ -836,7 +865,7 @@ int make_plan(const Shapes& s, Plan* plan) {
     }
     off = align256(off);
     P.off_items = off;
-    off = align256(off + (size_t)items * 16u);
+    off = align256(off + (size_t)items * 32u);
     P.off_count = off;
     off = align256(off + 4u);
     P.off_seq = off;

@@ -26,12 +26,14 @@ struct FwdParams {
     int64_t bt_s0;
     int32_t batch, H, Hk, G, D, page;
     int32_t total_q;
+    int32_t max_lk;         // paged: block_table width * page; non-paged: total_k
+    int32_t num_blocks;     // paged pool size (block ids are clamped into it)
     int32_t window_left, window_right;
     int32_t chunk;          // keys per split (split only if max_chunks > 1)
     int32_t max_chunks;
     int32_t rows;           // rows per work item (MFMA rows per wave * waves)
     int32_t items_bound;    // upper bound of the number of work items per K/V head
-    int4* items;            // work list written by the planner: {b, rt, c | nc<<16, 0}
+    int4* items;            // work list: per item {b, rt, c | nc<<16, 0}, {q0, Lq, k0, Lk}
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
