@@ -130,6 +130,55 @@ def stored_traffic(workload: str):
         return None
 
 
+def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib):
+    """Markdown summary of the main kernel's HBM traffic from rocprofv3 --pmc CSVs.
+
+    FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same
+    counter reads for a plain device copy of ``copy_mib`` MiB (read and write
+    of exactly that many bytes)."""
+    import csv
+
+    def per_kernel(path, counter):
+        vals = {}
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] == counter:
+                vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in vals.items()}
+
+    def main_kernel(d):
+        k = [n for n in d if "attn_fwd_kernel" in n]
+        assert k, "attention kernel not in counter file"
+        return k[0], d[k[0]]
+
+    copy_kib = copy_mib * 1024.0
+    cf = per_kernel(copy_fetch_csv, "FETCH_SIZE").get("__amd_rocclr_copyBuffer")
+    cw = per_kernel(copy_write_csv, "WRITE_SIZE").get("__amd_rocclr_copyBuffer")
+    f_scale, w_scale = copy_kib / cf, copy_kib / cw
+    name, fetch = main_kernel(per_kernel(fetch_csv, "FETCH_SIZE"))
+    _, write = main_kernel(per_kernel(write_csv, "WRITE_SIZE"))
+    traffic = (fetch * f_scale + write * w_scale) * 1024.0
+    import workloads as W
+    wl = W.make_config(workload)
+    alg = work_of(wl)["total_bytes"]
+    lines = [
+        "# HBM traffic of attn_fwd_kernel, workload %s" % workload,
+        "",
+        "Counters per dispatch (KiB), averaged over the profiled launches, scaled by a plain",
+        "%d MiB device copy (`__amd_rocclr_copyBuffer`) read with the same counters." % copy_mib,
+        "",
+        "- kernel: `%s`" % name,
+        "- kernel source sha256/16: `%s`" % kernel_sha(),
+        "- FETCH_SIZE per launch (raw KiB): `%.1f`" % fetch,
+        "- WRITE_SIZE per launch (raw KiB): `%.1f`" % write,
+        "- copy calibration FETCH_SIZE / WRITE_SIZE (KiB for %d KiB moved): `%.1f` / `%.1f`" % (copy_kib, cf, cw),
+        "- scale factors fetch / write: `%.4f` / `%.4f`" % (f_scale, w_scale),
+        "- HBM bytes per launch (scaled): `%.0f`" % traffic,
+        "- algorithmic bytes per launch: `%.0f`" % alg,
+        "- traffic / algorithmic: `%.3f`" % (traffic / alg),
+    ]
+    return "\n".join(lines) + "\n"
+
+
 # ----------------------------------------------------------------- CPU leg
 
 def cpu_baseline(wl, work, decode: bool):
@@ -199,7 +248,13 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
+                                                            "COPY_WRITE_CSV"),
+                    help="print the HBM-traffic summary of rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+    if args.counters_summary:
+        print(counters_summary(args.workload, *args.counters_summary, copy_mib=1024), end="")
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
