@@ -180,6 +180,7 @@ def test_no_visible_key_rows_are_zero(oracle_mod):
     dict(lq=[20, 8], lk=[20, 30], H=2, Hk=2, D=16, wl=4, wr=3),               # two-sided window
     dict(lq=[9, 14], lk=[31, 14], H=4, Hk=1, D=24, wl=-1, wr=-1),             # no mask, MQA
     dict(lq=[12, 4], lk=[5, 0], H=2, Hk=1, D=8, wl=-1, wr=0),                 # Lq > Lk, empty
+    dict(lq=[7, 19], lk=[30, 19], H=3, Hk=1, D=13, wl=5, wr=-1),              # odd head dim
 ])
 @pytest.mark.parametrize("paged", [False, True])
 def test_matches_torch_sdpa_fp64(oracle_mod, case, paged):

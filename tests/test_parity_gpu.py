@@ -65,8 +65,13 @@ SMALL = [
     ("decode-d512-mqa-q4", [4, 4, 4], [1100, 2500, 300], 16, 1, 512, 128, -1, 0),
     ("decode-d64-window", [2, 3, 1], [500, 90, 7], 8, 2, 64, 32, 50, 0),
     ("noncausal-two-sided", [37, 20], [50, 20], 4, 2, 128, 0, 7, 5),
-    ("odd-d80", [50, 10], [60, 10], 4, 2, 80, 0, -1, 0),
-    ("odd-d40-paged-decode", [1, 2], [77, 300], 4, 2, 40, 32, -1, 0),
+    ("d80", [50, 10], [60, 10], 4, 2, 80, 0, -1, 0),
+    ("d40-paged-decode", [1, 2], [77, 300], 4, 2, 40, 32, -1, 0),
+    # head dims that are not multiples of 8 take the element-wise load path
+    ("odd-d13", [33, 5], [40, 5], 4, 2, 13, 0, -1, 0),
+    ("odd-d100-paged", [70, 1], [90, 600], 4, 1, 100, 64, -1, 0),
+    ("odd-d200-decode", [2, 1], [700, 45], 8, 2, 200, 32, -1, 0),
+    ("odd-d500-decode", [4, 4], [300, 1300], 8, 1, 500, 128, -1, 0),
 ]
 
 
