@@ -11,6 +11,7 @@
 // divisibility, workspace) come after and carry their own texts.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdio>
@@ -293,6 +294,16 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
         for (int i = 0; i + 1 < t->rank; ++i) vec = vec && (t->stride[i] % 8 == 0);
     }
     p.vec = vec ? 1 : 0;
+    // the uniform-base copy path needs the padded head dim to be the real one and
+    // the per-lane byte offsets (up to 8 rows) to fit in 32 bits
+    {
+        const int dp = p.D <= 64 ? 64 : p.D <= 128 ? 128 : p.D <= 256 ? 256 : 512;
+        const int64_t krow = 2 * (paged ? k->stride[1] : k->stride[0]);
+        const int64_t vrow = 2 * (paged ? v->stride[1] : v->stride[0]);
+        p.k_rowb = (int32_t)std::min<int64_t>(krow, INT32_MAX);
+        p.v_rowb = (int32_t)std::min<int64_t>(vrow, INT32_MAX);
+        p.fast_copy = (vec && p.D == dp && 128 * krow + 2 * dp < INT32_MAX && 128 * vrow + 2 * dp < INT32_MAX) ? 1 : 0;
+    }
 
     rc = fa::launch_fwd(plan, p, stream, g_ev_start, g_ev_stop);
     if (rc) return fail(rc, "kernel launch failed: %s", fa::last_hip_error());

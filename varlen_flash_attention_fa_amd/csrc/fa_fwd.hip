@@ -96,11 +96,13 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int d0, int D, bool
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
 __device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
-    __bf16 x = static_cast<__bf16>(a);
-    __bf16 y = static_cast<__bf16>(b);
-    return (unsigned int)__builtin_bit_cast(unsigned short, x) |
-           ((unsigned int)__builtin_bit_cast(unsigned short, y) << 16);
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
 }
 
 __device__ __forceinline__ unsigned short to_bf16(float a) {
@@ -450,14 +452,53 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             if (paged) {
                 const int p0 = ts / P;
                 const int p1 = min(p0 + 1, (seg1 - 1) / P);  // only pages staged for this segment
-                pg0 = s_pages[p0 - pg_first];
-                pg1 = s_pages[p1 - pg_first];
+                pg0 = __builtin_amdgcn_readfirstlane(s_pages[p0 - pg_first]);
+                pg1 = __builtin_amdgcn_readfirstlane(s_pages[p1 - pg_first]);
                 base0 = p0 * P;
             }
             const int ln = opaque_lane();
             const int lrow = ln / CH;
             const int lpos = ln % CH;
-            if (vec) {
+            // Fast path for interior tiles: the RPI rows of one copy instruction lie in
+            // one page, so the address is a wave-uniform base (page, first row, head)
+            // plus a per-lane offset (row within the copy, swizzled chunk) that does
+            // not depend on the tile.  The swizzle splits as (lane part) ^ (uniform
+            // part) because the copy's first row is a multiple of RPI.
+            if (p.fast_copy && ts >= kb && ts + BN <= ke) {
+                const int xk = lpos ^ (lrow & SWK);
+                const int xv = lpos ^ ((2 * lrow) & SWV);
+                const unsigned lk_off = (unsigned)lrow * (unsigned)p.k_rowb;
+                const unsigned lv_off = (unsigned)lrow * (unsigned)p.v_rowb;
+                // per tile: byte pointers to row 0 of the tile's page(s) (paged) or to
+                // the tile's first row (packed); per copy: a 32-bit row offset
+                const unsigned char *kp0, *kp1, *vp0, *vp1;
+                int slot0 = 0;
+                if (paged) {
+                    kp0 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg0 * p.k_s0 + (int64_t)hk * p.k_s2);
+                    vp0 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg0 * p.v_s0 + (int64_t)hk * p.v_s2);
+                    kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg1 * p.k_s0 + (int64_t)hk * p.k_s2);
+                    vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg1 * p.v_s0 + (int64_t)hk * p.v_s2);
+                    slot0 = ts - base0;
+                } else {
+                    kp0 = kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)(it.k0 + ts) * p.k_s0 + (int64_t)hk * p.k_s1);
+                    vp0 = vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)(it.k0 + ts) * p.v_s0 + (int64_t)hk * p.v_s1);
+                }
+                const int wv = __builtin_amdgcn_readfirstlane(wave);  // lets the compiler keep bases scalar
+#pragma unroll
+                for (int i = 0; i < NI; ++i) {
+                    const int r0 = (wv * NI + i) * RPI;  // first row of this copy (uniform)
+                    int sl = slot0 + r0;
+                    const bool second = paged && sl >= P;
+                    sl = second ? sl - P : sl;
+                    const unsigned char* kb_ = (second ? kp1 : kp0) + (unsigned)sl * (unsigned)p.k_rowb;
+                    const unsigned char* vb_ = (second ? vp1 : vp0) + (unsigned)sl * (unsigned)p.v_rowb;
+                    const unsigned vk = lk_off + ((unsigned)(xk ^ (r0 & SWK)) << 4);
+                    const unsigned vv = lv_off + ((unsigned)(xv ^ ((2 * r0) & SWV)) << 4);
+                    unsigned char* dst = smem + (t % NS) * 2 * TILEB + (wv * NI + i) * 1024;
+                    copy16_to_lds(reinterpret_cast<const uint16_t*>(kb_ + vk), dst);
+                    copy16_to_lds(reinterpret_cast<const uint16_t*>(vb_ + vv), dst + TILEB);
+                }
+            } else if (vec) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int rr = (wave * NI + i) * RPI + lrow;

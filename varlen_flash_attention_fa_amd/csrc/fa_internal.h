@@ -37,6 +37,8 @@ struct FwdParams {
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
+    int32_t fast_copy;      // 1 = interior K/V tiles may use uniform-base + lane-offset copies
+    int32_t k_rowb, v_rowb; // bytes between consecutive key rows (paged: slot stride; packed: token stride)
     float scale_log2;       // softmax_scale * log2(e)
 };
 
