@@ -135,6 +135,7 @@ __device__ __forceinline__ Range row_range(const FwdParams& p, int i, int Lq, in
 // vmcnt bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0, "vmcnt");
     constexpr int n = N > 63 ? 63 : N;
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
 }
@@ -557,10 +558,18 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             if (t < ntiles) issue(t);
 
         for (int t = 0; t < ntiles; ++t) {
-            if (t + NS - 2 < ntiles) wait_vmcnt<(NS - 2) * 2 * NI>();
-            else wait_vmcnt<0>();
-            __syncthreads();  // tile t is in LDS for every wave; stage (t-1)%NS is free
-            if (t + NS - 1 < ntiles) issue(t + NS - 1);
+            if constexpr (NS == 1) {
+                // single stage: copy, wait, compute (latency is hidden by other waves)
+                __syncthreads();  // every wave is done with the previous tile
+                issue(t);
+                wait_vmcnt<0>();
+                __syncthreads();
+            } else {
+                if (t + NS - 2 < ntiles) wait_vmcnt<(NS >= 2 ? (NS - 2) * 2 * NI : 0)>();
+                else wait_vmcnt<0>();
+                __syncthreads();  // tile t is in LDS for every wave; stage (t-1)%NS is free
+                if (t + NS - 1 < ntiles) issue(t + NS - 1);
+            }
 
             const int n0 = seg0 + t * BN;
             const unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
@@ -841,12 +850,11 @@ hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
         else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32, 2>(plan, p, s);
         else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
     }
-    // decode: 16 rows per wave, keys split over work items
-    if (plan.wr == 1) {
-        if constexpr (DP <= 128) return launch_attn<DP, 16, 1, 32, 3>(plan, p, s);
-        else return launch_attn<DP, 16, 1, 32, 2>(plan, p, s);
-    }
-    return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
+    // decode: 16 rows per wave, keys split over work items, one LDS stage: HBM
+    // latency is hidden by the number of resident workgroups (LDS-limited),
+    // which beats deeper per-wave pipelines on this path
+    if (plan.wr == 1) return launch_attn<DP, 16, 1, 32, 1>(plan, p, s);
+    return launch_attn<DP, 16, 4, 32, 1>(plan, p, s);
 }
 
 int env_int(const char* name, int dflt) {
