@@ -286,6 +286,7 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
         p.items = reinterpret_cast<int4*>(ws + plan.off_items);
         p.item_count = reinterpret_cast<int32_t*>(ws + plan.off_count);
         p.seq_off = reinterpret_cast<int32_t*>(ws + plan.off_seq);
+        p.tok_nc = reinterpret_cast<int32_t*>(ws + plan.off_tok);
     }
     // 16-byte vector access is legal when every row start is 16-byte aligned
     bool vec = (p.D % 8 == 0);

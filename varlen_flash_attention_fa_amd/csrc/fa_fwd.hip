@@ -204,7 +204,7 @@ __device__ __forceinline__ SeqSpan seq_span(const FwdParams& p, int b) {
 // and the short ones fill the tail.
 constexpr int kPlanThreads = 1024;
 constexpr int kCostBuckets = 128;
-constexpr int kLdsSeqs = 4096;
+constexpr int kLdsSeqs = 2048;  // sequences whose spans and item offsets stay in LDS
 
 __device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk) {
     return p.max_chunks > 1 ? min(p.max_chunks, max(1, ceil_div(lk, p.chunk))) : 1;
@@ -219,34 +219,52 @@ __device__ __forceinline__ int cost_bucket(int64_t cost) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     __shared__ int s_off_lds[kLdsSeqs + 1];
-    __shared__ int s_scan[kPlanThreads];
+    __shared__ int4 s_span[kLdsSeqs];
+    __shared__ int s_wsum[kPlanThreads / 64];
     __shared__ int s_hist[kCostBuckets];
     const int tid = threadIdx.x;
-    int* off = p.batch <= kLdsSeqs ? s_off_lds : p.seq_off;
+    const int lane = tid & 63, wave = tid >> 6;
+    const bool cached = p.batch <= kLdsSeqs;
+    int* off = cached ? s_off_lds : p.seq_off;
     const bool split = p.max_chunks > 1;
     const int R = p.rows;
 
     for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_hist[i] = 0;
+    if (split)  // split partials: chunks per token for the combine (0 = not in a sequence)
+        for (int t = tid; t < p.total_q; t += kPlanThreads) p.tok_nc[t] = 0;
 
-    // items per sequence -> exclusive offsets off[0..batch]
+    // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
+    // LDS step per 1024 sequences)
     int carry = 0;
     for (int base = 0; base < p.batch; base += kPlanThreads) {
         const int b = base + tid;
         int cnt = 0;
         if (b < p.batch) {
             const SeqSpan sp = seq_span(p, b);
+            if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk);
         }
-        s_scan[tid] = cnt;
-        __syncthreads();
-        for (int o = 1; o < kPlanThreads; o <<= 1) {
-            const int x = tid >= o ? s_scan[tid - o] : 0;
-            __syncthreads();
-            s_scan[tid] += x;
-            __syncthreads();
+        int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
         }
-        if (b < p.batch) off[b] = carry + s_scan[tid] - cnt;
-        carry += s_scan[kPlanThreads - 1];
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        if (wave == 0) {
+            int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
+#pragma unroll
+            for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
+                const int y = __shfl_up(w, o, 64);
+                if (lane >= o) w += y;
+            }
+            if (lane < kPlanThreads / 64) s_wsum[lane] = w;
+        }
+        __syncthreads();
+        const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
+        if (b < p.batch) off[b] = carry + incl - cnt;
+        carry += s_wsum[kPlanThreads / 64 - 1];
         __syncthreads();
     }
     const int total = min(carry, p.items_bound);
@@ -255,6 +273,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
         *p.item_count = total;
     }
     __syncthreads();
+    if (split)
+        for (int b = tid; b < p.batch; b += kPlanThreads) {
+            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+            const int nc = seq_chunks(p, sp.Lk);
+            for (int t = sp.q0; t < sp.q0 + sp.Lq; ++t) p.tok_nc[t] = nc;
+        }
 
     // decode item i -> (b, rt, c, nc, cost bucket); the first pass counts
     // buckets, the second places each item at its bucket's next slot
@@ -266,7 +290,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 if (off[mid] <= i) lo = mid; else hi = mid;
             }
             const int b = lo;
-            const SeqSpan sp = seq_span(p, b);
+            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
             const int lq = sp.Lq, lk = sp.Lk;
             const int nc = seq_chunks(p, lk);
             const int local = i - off[b];
@@ -779,16 +803,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int t = blockIdx.x;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (h >= p.H) return;
-    // sequence of token t: last b with cu_q[b] <= t
-    int lo = 0, hi = p.batch;  // answer in [0, batch)
-    if (t >= p.cu_q[p.batch]) return;
-    while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (p.cu_q[mid] <= t) lo = mid; else hi = mid;
-    }
-    const int b = lo;
-    const int Lk = seq_span(p, b).Lk;
-    const int nc = min(p.max_chunks, max(1, ceil_div(Lk, p.chunk)));
+    const int nc = p.tok_nc[t];  // chunks of this token's sequence (planner), 0 if none
     if (nc <= 1) return;
     const float* pl = p.part_lse + (int64_t)t * p.H + h;
     const int64_t cstride_l = (int64_t)p.total_q * p.H;
@@ -919,6 +934,8 @@ int make_plan(const Shapes& s, Plan* plan) {
     off = align256(off + 4u);
     P.off_seq = off;
     off = align256(off + (size_t)(s.batch + 1) * 4u);
+    P.off_tok = off;
+    if (P.max_chunks > 1) off = align256(off + (size_t)s.total_q * 4u);
     P.ws_bytes = off;
     *plan = P;
     return 0;

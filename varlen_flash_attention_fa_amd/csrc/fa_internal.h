@@ -36,6 +36,7 @@ struct FwdParams {
     int4* items;            // work list: per item {b, rt, c | nc<<16, 0}, {q0, Lq, k0, Lk}
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
+    int32_t* tok_nc;        // [total_q] chunks of each token's sequence (split only)
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
     int32_t fast_copy;      // 1 = interior K/V tiles may use uniform-base + lane-offset copies
     int32_t k_rowb, v_rowb; // bytes between consecutive key rows (paged: slot stride; packed: token stride)
@@ -54,7 +55,7 @@ struct Plan {
     int chunk;      // keys per split
     int max_chunks; // upper bound of splits per sequence
     int64_t items_bound;  // upper bound of work items per K/V head
-    size_t off_items, off_count, off_seq;  // workspace layout (bytes)
+    size_t off_items, off_count, off_seq, off_tok;  // workspace layout (bytes)
     size_t ws_bytes;
 };
 
