@@ -860,8 +860,10 @@ hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
 
 template <int DP>
 hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
+    // one LDS stage here too: it frees registers and LDS for 3 resident workgroups
+    // per CU, which beat a prefetching second stage (+6-8% on long prefill)
     if (plan.kind == KIND_PREFILL) {
-        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64, 2>(plan, p, s);
+        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64, 1>(plan, p, s);
         else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32, 2>(plan, p, s);
         else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
     }
