@@ -904,6 +904,25 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.bn = P.dp <= 128 ? 64 : 32;
         P.chunk = INT_MAX;
         P.max_chunks = 1;
+        // Few row tiles over long key ranges (chunked prefill on a long cache) give
+        // too few, too uneven work items for the chip: cut the keys into halves of
+        // the longest range (at least 4096 keys), merged by the combine kernel.
+        // Smaller chunks balance better but their partials cost more than they save.
+        const int64_t rows = (int64_t)P.mr * P.wr;
+        const int64_t items = ((s.total_q * G + rows - 1) / rows + s.batch) * s.Hk;
+        int64_t chunk = 0;
+        if (items < 3072 && s.max_lk >= 8192)
+            chunk = std::max<int64_t>(4096, (s.max_lk / 2 + P.bn - 1) / P.bn * P.bn);
+        chunk = env_int("FA_SPLIT_KEYS", (int)chunk);
+        if (chunk > 0) {
+            chunk = std::max<int64_t>(P.bn, (chunk + P.bn - 1) / P.bn * P.bn);
+            const int64_t mc = (s.max_lk + chunk - 1) / chunk;
+            if (mc > 4096) return FA_ERR_ARGUMENT;
+            if (mc > 1) {
+                P.chunk = (int)chunk;
+                P.max_chunks = (int)mc;
+            }
+        }
     } else {
         P.mr = 16;
         P.wr = rows_avg <= 16 ? 1 : 4;
