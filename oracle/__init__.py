@@ -45,6 +45,10 @@ def _load():
                       ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int,
                       ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int]
         f.restype = ctypes.c_int
+        g = lib.fa_oracle_kv_append
+        g.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P,
+                      ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, P]
+        g.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -120,3 +124,25 @@ def attention_workload(wl, token_sel=None, nthreads=None):
     return attention(wl.q, wl.k, wl.v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.block_table,
                      wl.page_block_size, wl.softmax_scale, wl.window_left, wl.window_right,
                      token_sel=token_sel, nthreads=nthreads)
+
+
+def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_pool, v_pool):
+    """Reference paged K/V append; returns new (k_pool, v_pool) uint16 arrays (inputs untouched).
+
+    k_new/v_new (total_new, Hk, D) bf16; pools (num_blocks, P, Hk, D) bf16; new token j
+    of sequence b goes to logical position Lk_b - Lnew_b + j.
+    """
+    lib = _load()
+    kn, vn = _bits(k_new), _bits(v_new)
+    kp, vp = _bits(k_pool).copy(), _bits(v_pool).copy()
+    assert kn.ndim == 3 and kn.shape == vn.shape and kp.ndim == 4 and kp.shape == vp.shape
+    cu_n = np.ascontiguousarray(cu_seqlens_new, dtype=np.int32)
+    cu_k = np.ascontiguousarray(cu_seqlens_k, dtype=np.int32)
+    bt = np.ascontiguousarray(block_table, dtype=np.int32)
+    rc = lib.fa_oracle_kv_append(kn.ctypes.data, vn.ctypes.data, kn.shape[0], kn.shape[1], kn.shape[2],
+                                 cu_n.ctypes.data, cu_k.ctypes.data, cu_n.shape[0] - 1,
+                                 bt.ctypes.data, bt.shape[1], kp.shape[1], kp.shape[0],
+                                 kp.ctypes.data, vp.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle kv_append rejected its arguments (code %d)" % rc)
+    return kp, vp

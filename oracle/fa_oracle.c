@@ -207,3 +207,41 @@ int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int h
     if (J.error == 2) return -3;
     return 0;
 }
+
+/*
+ * Paged K/V cache append (the write that precedes paged attention): the new
+ * tokens of sequence b are its last Lnew_b keys, i.e. new token j sits at
+ * logical key position  pos = Lk_b - Lnew_b + j  with  Lk_b = cu_k[b+1]-cu_k[b]
+ * (lengths after the append) and  Lnew_b = cu_new[b+1]-cu_new[b];  it is
+ * written to block block_table[b][pos / page], slot pos % page, for every K/V
+ * head.  Same block-table addressing as the attention's paged reads (page
+ * "flash-attn-varlen paged expects k/v tensors of rank 4", What it means;
+ * page "page_block_size ... does not match k shape", What it means).
+ *
+ *   k_new, v_new [total_new][Hk][D] bf16 bits;  k_pool, v_pool
+ *   [num_blocks][page][Hk][D] bf16 bits, updated in place.
+ * Returns 0, -1 for bad arguments, -2 when a position or block id falls
+ * outside the table or the pool (nothing is written for that token).
+ */
+int fa_oracle_kv_append(const uint16_t *k_new, const uint16_t *v_new, int64_t total_new, int num_heads_k,
+                        int head_dim, const int32_t *cu_new, const int32_t *cu_k, int batch,
+                        const int32_t *block_table, int bt_width, int page, int64_t num_blocks,
+                        uint16_t *k_pool, uint16_t *v_pool) {
+    if (batch < 0 || page <= 0 || num_heads_k <= 0 || head_dim <= 0) return -1;
+    const int64_t row = (int64_t)num_heads_k * head_dim;
+    int rc = 0;
+    for (int b = 0; b < batch; ++b) {
+        const int64_t n0 = cu_new[b], lnew = (int64_t)cu_new[b + 1] - cu_new[b];
+        const int64_t lk = (int64_t)cu_k[b + 1] - cu_k[b];
+        for (int64_t j = 0; j < lnew; ++j) {
+            const int64_t pos = lk - lnew + j;
+            if (n0 + j < 0 || n0 + j >= total_new || pos < 0 || pos / page >= bt_width) { rc = -2; continue; }
+            const int64_t blk = block_table[(int64_t)b * bt_width + pos / page];
+            if (blk < 0 || blk >= num_blocks) { rc = -2; continue; }
+            const int64_t dst = (blk * page + pos % page) * row;
+            memcpy(k_pool + dst, k_new + (n0 + j) * row, (size_t)row * sizeof(uint16_t));
+            memcpy(v_pool + dst, v_new + (n0 + j) * row, (size_t)row * sizeof(uint16_t));
+        }
+    }
+    return rc;
+}
