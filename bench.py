@@ -19,6 +19,10 @@ Prints ONE JSON line: metric/value/unit, ms_per_step, a ``roofline`` object
 for the main kernel (algorithmic bytes or FLOP per launch / its mean duration
 vs. the chip's peak) and a ``cpu_baseline`` object (the fp64 oracle timed on a
 bounded sample of the same workload on this host's cores).
+
+``--op append`` times the paged K/V append instead (``fa_kv_append``): each
+sequence of a paged workload appends as many new tokens as it has query rows
+(its last keys), reported as GB/s of algorithmic HBM traffic.
 """
 from __future__ import annotations
 
@@ -42,6 +46,8 @@ PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 DECODE = {"c2", "c5a", "c5b"}
 KERNEL_SRC = os.path.join(ROOT, "varlen_flash_attention_fa_amd", "csrc", "fa_fwd.hip")
+APPEND_SRC = os.path.join(ROOT, "varlen_flash_attention_fa_amd", "csrc", "fa_append.hip")
+APPEND_METRIC = "paged KV-cache append: GB/s of algorithmic HBM traffic (%HBM)"
 
 
 # ------------------------------------------------------------------ HIP events
@@ -109,13 +115,27 @@ def work_of(wl):
 
 # ------------------------------------------------------------------- profiles
 
-def kernel_sha() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_sha(src: str = KERNEL_SRC) -> str:
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
+def append_work(wl):
+    """Algorithmic bytes of appending each sequence's query-length worth of new tokens."""
+    Hk, D = wl.num_heads_k, wl.head_dim
+    total_new = float(wl.lens_q.sum())
+    rows = 2.0 * total_new * Hk * D * 2          # K and V rows, bf16
+    meta = 8.0 * (wl.batch + 1) + 4.0 * total_new  # cu arrays + one block id per token
+    return dict(total_new=int(total_new), row_bytes=rows, total_bytes=2.0 * rows + meta)
+
+
+def stored_traffic(workload: str, op: str = "fwd"):
     """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
-    path = os.path.join(ROOT, "profiles", "attn_fwd_%s_hbm_traffic.md" % workload)
+    if op == "append":
+        path = os.path.join(ROOT, "profiles", "kv_append_%s_hbm_traffic.md" % workload)
+        src = APPEND_SRC
+    else:
+        path = os.path.join(ROOT, "profiles", "attn_fwd_%s_hbm_traffic.md" % workload)
+        src = KERNEL_SRC
     if not os.path.exists(path):
         return None
     vals = {}
@@ -123,7 +143,7 @@ def stored_traffic(workload: str):
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             vals[k.strip()] = v.strip().strip("`")
-    if vals.get("kernel source sha256/16") != kernel_sha():
+    if vals.get("kernel source sha256/16") != kernel_sha(src):
         return None
     try:
         return float(vals["HBM bytes per launch (scaled)"])
@@ -131,7 +151,7 @@ def stored_traffic(workload: str):
         return None
 
 
-def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib):
+def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv, copy_mib, op="fwd"):
     """Markdown summary of the main kernel's HBM traffic from rocprofv3 --pmc CSVs.
 
     FETCH_SIZE / WRITE_SIZE (KiB per dispatch) are scaled by what the same
@@ -146,9 +166,11 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
                 vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         return {k: sum(v) / len(v) for k, v in vals.items()}
 
+    kname = "kv_append_kernel" if op == "append" else "attn_fwd_kernel"
+
     def main_kernel(d):
-        k = [n for n in d if "attn_fwd_kernel" in n]
-        assert k, "attention kernel not in counter file"
+        k = [n for n in d if kname in n]
+        assert k, kname + " not in counter file"
         return k[0], d[k[0]]
 
     copy_kib = copy_mib * 1024.0
@@ -159,16 +181,18 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
     _, write = main_kernel(per_kernel(write_csv, "WRITE_SIZE"))
     traffic = (fetch * f_scale + write * w_scale) * 1024.0
     import workloads as W
-    wl = W.make_config(workload)
-    alg = work_of(wl)["total_bytes"]
+    if op == "append":
+        alg = append_work(W.append_config(workload))["total_bytes"]
+    else:
+        alg = work_of(W.make_config(workload))["total_bytes"]
     lines = [
-        "# HBM traffic of attn_fwd_kernel, workload %s" % workload,
+        "# HBM traffic of %s, workload %s%s" % (kname, workload, " (append)" if op == "append" else ""),
         "",
         "Counters per dispatch (KiB), averaged over the profiled launches, scaled by a plain",
         "%d MiB device copy (`__amd_rocclr_copyBuffer`) read with the same counters." % copy_mib,
         "",
         "- kernel: `%s`" % name,
-        "- kernel source sha256/16: `%s`" % kernel_sha(),
+        "- kernel source sha256/16: `%s`" % kernel_sha(APPEND_SRC if op == "append" else KERNEL_SRC),
         "- FETCH_SIZE per launch (raw KiB): `%.1f`" % fetch,
         "- WRITE_SIZE per launch (raw KiB): `%.1f`" % write,
         "- copy calibration FETCH_SIZE / WRITE_SIZE (KiB for %d KiB moved): `%.1f` / `%.1f`" % (copy_kib, cf, cw),
@@ -237,6 +261,131 @@ def cpu_baseline(wl, work, decode: bool):
             "sample": "%d of %d query rows (seeded), %.3g GFLOP, %.2f s" % (n, T, flops / 1e9, dt)}
 
 
+# ------------------------------------------------------------- append bench
+
+def cpu_append_baseline(wl, k_new, v_new, work):
+    """Time the oracle's append of the whole workload, repeated for >= 3 s."""
+    import oracle
+    oracle.build()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.kv_append(k_new, v_new, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.block_table, wl.k, wl.v)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= 3.0:
+            break
+    return {"value": round(reps * work["total_bytes"] / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": "whole append (%d tokens) run %d times in %.2f s; each oracle call also copies "
+                      "both pools (it returns new ones)" % (work["total_new"], reps, dt)}
+
+
+def bench_append(args, fa, W, hip, dev, stream):
+    import torch
+    print("bench: generating %s (append)" % args.workload, file=sys.stderr, flush=True)
+    wl = W.append_config(args.workload, args.seed)
+    work = append_work(wl)
+    # new rows: the pool rows of each sequence's last Lq keys (what a decode or
+    # chunked-prefill step appends); rotated copies keep them out of the MALL
+    P = wl.page_block_size
+    rows = []
+    for b in range(wl.batch):
+        pos = np.arange(int(wl.lens_k[b] - wl.lens_q[b]), int(wl.lens_k[b]))
+        rows.append(wl.block_table[b, pos // P].astype(np.int64) * P + pos % P)
+    rows = torch.from_numpy(np.concatenate(rows))
+    Hk, D = wl.num_heads_k, wl.head_dim
+    k_new = wl.k.view(-1, Hk, D)[rows].contiguous()
+    v_new = wl.v.view(-1, Hk, D)[rows].contiguous()
+    n_new = int(min(32, max(2, math.ceil(1.0e9 / max(1.0, work["row_bytes"])))))
+    with torch.cuda.stream(stream):
+        news = [(k_new.to(dev), v_new.to(dev)) for _ in range(n_new)]
+        pools = [(wl.k.to(dev), wl.v.to(dev)) for _ in range(2)]
+        cu_n = torch.from_numpy(wl.cu_seqlens_q).to(dev)
+        cu_k = torch.from_numpy(wl.cu_seqlens_k).to(dev)
+        bt = torch.from_numpy(wl.block_table).to(dev)
+        torch.cuda.synchronize()
+    dnew = [(fa._tdesc(a), fa._tdesc(b)) for a, b in news]
+    dpool = [(fa._tdesc(a), fa._tdesc(b)) for a, b in pools]
+    dbt = fa._tdesc(bt)
+    sh = stream.cuda_stream
+
+    def step(i, ev_k=None):
+        kn, vn = dnew[i % n_new]
+        kc, vc = dpool[i % 2]
+        if ev_k is not None:
+            fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
+        rc = fa.fa_kv_append(kn, vn, cu_n.data_ptr(), cu_k.data_ptr(), wl.batch, dbt, kc, vc, P, sh)
+        if rc:
+            raise RuntimeError(fa.fa_last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # A step is this one kernel: two events around the whole timed region give its
+    # mean duration without the per-call event cost (a few us, comparable to the
+    # kernel on the small appends).  Sampled per-call events are kept as detail.
+    K = args.steps
+    every = max(1, args.event_every)
+    sampled = [i for i in range(K) if i % every == every // 2] or [K // 2]
+    region_k = (hip.event(), hip.event())
+    print("bench: timing %d append steps" % K, file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hip.record(region_k[0], sh)
+    for i in range(K):
+        step(i)
+    hip.record(region_k[1], sh)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kern_mean = hip.elapsed_ms(*region_k) / K
+    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
+    for i in sampled:
+        step(i, ev_kern[i])
+        fa.fa_varlen_set_kernel_events(0, 0)
+    torch.cuda.synchronize()
+    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
+    for a, b in list(ev_kern.values()) + [region_k]:
+        hip.destroy(a)
+        hip.destroy(b)
+    # the pools must still equal the original (the new rows are the original rows)
+    for kc, vc in pools:
+        assert torch.equal(kc.view(torch.int16).cpu(), wl.k.view(torch.int16)), "append changed the K pool"
+        assert torch.equal(vc.view(torch.int16).cpu(), wl.v.view(torch.int16)), "append changed the V pool"
+    achieved = work["total_bytes"] / (kern_mean * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(args.workload, "append")}
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle append)", file=sys.stderr, flush=True)
+        cpu = cpu_append_baseline(wl, k_new, v_new, work)
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": APPEND_METRIC,
+        "value": round(work["total_bytes"] / (ms_per_step * 1e-3) / 1e9, 3),
+        "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16, seed %d)" % wl.seed,
+        "config": {
+            "workload": "append into %s: %s" % (args.workload, wl.extra.get("desc", "")),
+            "batch": wl.batch, "total_new": work["total_new"], "num_heads_k": Hk, "head_dim": D,
+            "page_block_size": P, "parallelism": "single GPU",
+        },
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {
+            "append_kernel_ms_mean": round(kern_mean, 6),
+            "append_kernel_ms_per_call_events_p50": round(float(np.median(kern_ms)), 6),
+            "per_call_event_samples": len(sampled), "algorithmic_total_bytes": work["total_bytes"],
+            "new_row_copies_rotated": n_new, "kernel_source_sha256_16": kernel_sha(APPEND_SRC),
+            "device": props.name,
+        },
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------- main
 
 def main(argv=None):
@@ -246,6 +395,8 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--op", default="fwd", choices=["fwd", "append"],
+                    help="fwd: the attention forward (default); append: the paged K/V append")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8, metavar="N",
                     help="bracket the call and its main kernel with HIP events on every N-th timed "
@@ -257,7 +408,7 @@ def main(argv=None):
                     help="print the HBM-traffic summary of rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
     if args.counters_summary:
-        print(counters_summary(args.workload, *args.counters_summary, copy_mib=1024), end="")
+        print(counters_summary(args.workload, *args.counters_summary, copy_mib=1024, op=args.op), end="")
         return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -285,6 +436,8 @@ def main(argv=None):
 
     fa.load()
     hip = Hip()
+    if args.op == "append":
+        return bench_append(args, fa, W, hip, dev, stream)
     print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
     wl = W.make_config(args.workload, args.seed)
     work = work_of(wl)

@@ -1,10 +1,11 @@
 /*
  * fa_varlen.h -- C ABI of the MI355X (gfx950) varlen flash-attention forward.
  *
- * One operation: the forward pass of softmax attention over sequences packed
- * back to back ("varlen"), with grouped-query heads, a softmax scale, a
- * left/right key window around the bottom-right aligned diagonal, and an
- * optional paged K/V cache read through a per-sequence block table.
+ * The forward pass of softmax attention over sequences packed back to back
+ * ("varlen"), with grouped-query heads, a softmax scale, a left/right key
+ * window around the bottom-right aligned diagonal, and an optional paged K/V
+ * cache read through a per-sequence block table; plus the append that writes
+ * new tokens' K/V into such a paged cache.
  *
  * The operation and its argument contract are those of candle's
  * FlashAttentionVarLen forward (huggingface/candle, candle-flash-attn), as the
@@ -137,12 +138,53 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * fa_kv_append_check -- the contract of fa_kv_append alone (host code, no GPU
+ * needed, no pointer dereferenced).  Returns FA_OK or the first failing check.
+ */
+int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t batch,
+                       const fa_tensor* block_table, const fa_tensor* k_cache,
+                       const fa_tensor* v_cache, int32_t page_block_size);
+
+/*
+ * fa_kv_append -- enqueue on `stream` the write that fills a paged K/V cache
+ * before a paged fa_varlen_fwd reads it: each new token's K and V rows are
+ * scattered into the pool block and slot that its sequence's block table names.
+ * Addressing is the paged read's (pages "flash-attn-varlen paged expects k/v
+ * tensors of rank 4" and "page_block_size ... does not match k shape", What it
+ * means: logical key n of sequence b is block block_table[b][n / P], slot n % P).
+ *
+ *   k_new, v_new   (total_new, num_heads_k, head_dim) bf16, last dim contiguous,
+ *                  same shape; read only.
+ *   cu_seqlens_new device int32 [batch+1], cumulative new-token counts from 0:
+ *                  sequence b owns rows [cu_new[b], cu_new[b+1]) of k_new/v_new.
+ *   cu_seqlens_k   device int32 [batch+1], cumulative key counts AFTER the append
+ *                  (the array the following fa_varlen_fwd takes).  The new tokens
+ *                  are each sequence's last keys: new token j of sequence b goes to
+ *                  logical position Lk_b - Lnew_b + j.
+ *   block_table    int32 (batch, max_blocks), last dim contiguous.
+ *   k_cache, v_cache  (num_blocks, page_block_size, num_heads_k, head_dim) bf16,
+ *                  last dim contiguous, same shape; written in place.
+ *   page_block_size  must equal k_cache.shape[1] and be a multiple of 32; the
+ *                  head size is at most 512 (the paged forward's rules and texts).
+ * Every other element of the pools is left untouched.  A token whose position
+ * falls outside [0, max_blocks * P), whose block id falls outside the pool, or
+ * that lies in no sequence's range, is skipped (nothing is written for it).
+ * Overlapping targets (two tokens mapped to one slot) leave either one's row.
+ * Ownership and errors as for fa_varlen_fwd; the call is asynchronous and
+ * allocates nothing.  total_new * num_heads_k * head_dim must be below 2^31.
+ */
+int fa_kv_append(const fa_tensor* k_new, const fa_tensor* v_new, const int32_t* cu_seqlens_new,
+                 const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
+                 const fa_tensor* k_cache, const fa_tensor* v_cache, int32_t page_block_size,
+                 void* stream);
+
+/*
  * fa_varlen_set_kernel_events -- measurement hook for benchmarks.  With both
  * arguments non-NULL (hipEvent_t handles created by the caller), every later
- * fa_varlen_fwd on this thread records `start_event` immediately before and
- * `stop_event` immediately after its main attention kernel, on the call's
- * stream, so the caller can read that kernel's duration with
- * hipEventElapsedTime.  NULL, NULL turns it off.  The events stay owned by the
+ * fa_varlen_fwd (fa_kv_append) on this thread records `start_event`
+ * immediately before and `stop_event` immediately after its main attention
+ * kernel (its append kernel), on the call's stream, so the caller can read
+ * that kernel's duration with hipEventElapsedTime.  NULL, NULL turns it off.  The events stay owned by the
  * caller.  Always returns FA_OK.
  */
 int fa_varlen_set_kernel_events(void* start_event, void* stop_event);

@@ -126,11 +126,13 @@ def attention_workload(wl, token_sel=None, nthreads=None):
                      token_sel=token_sel, nthreads=nthreads)
 
 
-def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_pool, v_pool):
+def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_pool, v_pool, strict=True):
     """Reference paged K/V append; returns new (k_pool, v_pool) uint16 arrays (inputs untouched).
 
     k_new/v_new (total_new, Hk, D) bf16; pools (num_blocks, P, Hk, D) bf16; new token j
-    of sequence b goes to logical position Lk_b - Lnew_b + j.
+    of sequence b goes to logical position Lk_b - Lnew_b + j.  A token whose position or
+    block id falls outside the table or the pool is skipped; with ``strict`` that raises
+    ValueError instead of returning.
     """
     lib = _load()
     kn, vn = _bits(k_new), _bits(v_new)
@@ -143,6 +145,6 @@ def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_pool, v
                                  cu_n.ctypes.data, cu_k.ctypes.data, cu_n.shape[0] - 1,
                                  bt.ctypes.data, bt.shape[1], kp.shape[1], kp.shape[0],
                                  kp.ctypes.data, vp.ctypes.data)
-    if rc != 0:
+    if rc == -1 or (rc != 0 and strict):
         raise ValueError("oracle kv_append rejected its arguments (code %d)" % rc)
     return kp, vp

@@ -236,3 +236,65 @@ def test_workspace_bytes(lib):
     with pytest.raises(fa.FlashAttnError) as e:
         fa.fa_varlen_workspace_bytes(Q, K3, desc([86, 2, 32]), 3, None, 0)
     assert e.value.status == "FA_ERR_SHAPE"
+
+
+# ------------------------------------------------------------ paged append
+
+KN = desc([6, 2, 64])
+KC = desc([10, 32, 2, 64])
+BT3 = desc([3, 4], dtype=FA_DTYPE_I32)
+
+
+def acheck(kn=KN, vn=KN, batch=3, bt=BT3, kc=KC, vc=KC, page=32):
+    rc = fa.fa_kv_append_check(kn, vn, batch, bt, kc, vc, page)
+    return rc, fa.fa_last_error() if rc else ""
+
+
+def test_append_valid(lib):
+    assert acheck() == (0, "")
+    assert acheck(kn=desc([0, 2, 64]), vn=desc([0, 2, 64]))[0] == 0
+    assert acheck(batch=0, bt=desc([0, 4], dtype=FA_DTYPE_I32))[0] == 0
+
+
+def test_append_reuses_paged_page_rules(lib):
+    code, t, _ = tmpl("paged flash-attn requires page_block_size")
+    assert acheck(page=0) == (code, t)
+    code, t, _ = tmpl("page_block_size {")
+    assert acheck(page=64) == (code, render(t, page_block_size_arg="64", _seq=[dl([10, 32, 2, 64])]))
+    code, t, _ = tmpl("paged flash-attn requires page_block_size to be")
+    k = desc([10, 48, 2, 64])
+    assert acheck(kc=k, vc=k, page=48) == (code, render(t, page_block_size="48"))
+    code, t, _ = tmpl("paged flash-attn supports head sizes")
+    kn, kc = desc([6, 1, 520]), desc([4, 32, 1, 520])
+    assert acheck(kn=kn, vn=kn, kc=kc, vc=kc) == (code, render(t, head_size_og="520"))
+    kn, kc = desc([6, 1, 512]), desc([4, 32, 1, 512])
+    assert acheck(kn=kn, vn=kn, kc=kc, vc=kc)[0] == 0
+
+
+def test_append_shape_rank_dtype_contiguity(lib):
+    rank = {v: k for k, v in fa.STATUS.items()}
+    assert acheck(kn=desc([6, 2, 64, 1]))[0] == rank["FA_ERR_RANK"]
+    assert acheck(kc=desc([10, 32, 128]))[0] == rank["FA_ERR_RANK"]
+    assert acheck(kn=desc([6, 2, 64], dtype=FA_DTYPE_I32))[0] == rank["FA_ERR_DTYPE"]
+    assert acheck(bt=desc([3, 4]))[0] == rank["FA_ERR_DTYPE"]
+    rc, msg = acheck(kn=desc([6, 2, 64], stride=[128, 64, 2]))
+    assert rc == rank["FA_ERR_CONTIGUOUS"] and msg.startswith("the last dim of k_new must be contiguous")
+    code, t, _ = tmpl("the last dim of k must")
+    rc, msg = acheck(kc=desc([10, 32, 2, 64], stride=[8192, 256, 128, 2]))
+    assert rc == code and msg == render(t, k_stride=dl([8192, 256, 128, 2]))
+    code, t, _ = tmpl("shape mismatch k {:?} and v")
+    rc, msg = acheck(vc=desc([11, 32, 2, 64]))
+    assert rc == code and msg == render(t, _seq=[dl([10, 32, 2, 64]), dl([11, 32, 2, 64])])
+    assert acheck(vn=desc([5, 2, 64]))[0] == rank["FA_ERR_SHAPE"]
+    assert acheck(kn=desc([6, 1, 64]), vn=desc([6, 1, 64]))[0] == rank["FA_ERR_SHAPE"]
+    assert acheck(bt=desc([2, 4], dtype=FA_DTYPE_I32))[0] == rank["FA_ERR_SHAPE"]
+    code, t, _ = tmpl("block_table last dimension")
+    assert acheck(bt=desc([3, 4], stride=[8, 2], dtype=FA_DTYPE_I32)) == (code, t)
+    assert acheck(batch=-1)[0] == rank["FA_ERR_ARGUMENT"]
+    assert acheck(bt=None)[0] == rank["FA_ERR_ARGUMENT"]
+
+
+def test_append_empty_call_needs_no_gpu(lib):
+    """batch 0 or no new tokens: nothing is launched, no device pointer is inspected."""
+    assert fa.fa_kv_append(desc([0, 2, 64]), desc([0, 2, 64]), 0, 0, 3, BT3, KC, KC, 32, 0) == 0
+    assert fa.fa_kv_append(KN, KN, 0, 0, 0, desc([0, 4], dtype=FA_DTYPE_I32), KC, KC, 32, 0) == 0

@@ -6,8 +6,9 @@ device memory and the current stream.  There is no CPU fallback: if the shared
 library has not been built, importing the low-level functions raises.
 
 Low-level names mirror the C ABI (``fa_varlen_check``, ``fa_varlen_workspace_bytes``,
-``fa_varlen_fwd``, ``fa_last_error``) and take :class:`FaTensor` descriptors;
-:func:`varlen_fwd` is the tensor-level convenience wrapper.
+``fa_varlen_fwd``, ``fa_kv_append_check``, ``fa_kv_append``, ``fa_last_error``) and
+take :class:`FaTensor` descriptors; :func:`varlen_fwd` and :func:`kv_append` are the
+tensor-level convenience wrappers.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "FaTensor", "FlashAttnError", "lib_path", "load", "fa_varlen_check",
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
-    "fa_varlen_set_kernel_events",
+    "fa_varlen_set_kernel_events", "fa_kv_append_check", "fa_kv_append", "kv_append",
     "FA_DTYPE_BF16", "FA_DTYPE_I32", "STATUS",
 ]
 
@@ -75,6 +76,11 @@ def load():
     lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_varlen_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_varlen_set_kernel_events.restype = ctypes.c_int
+    lib.fa_kv_append_check.argtypes = [P, P, ctypes.c_int32, P, P, P, ctypes.c_int32]
+    lib.fa_kv_append_check.restype = ctypes.c_int
+    lib.fa_kv_append.argtypes = [P, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, P, P, P,
+                                 ctypes.c_int32, ctypes.c_void_p]
+    lib.fa_kv_append.restype = ctypes.c_int
     lib.fa_last_error.argtypes = []
     lib.fa_last_error.restype = ctypes.c_char_p
     _lib = lib
@@ -150,6 +156,49 @@ def fa_varlen_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqle
 def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:
     """Measurement hook: bracket the main kernel of later calls with these hipEvent_t handles."""
     return load().fa_varlen_set_kernel_events(start_event or None, stop_event or None)
+
+
+def fa_kv_append_check(k_new: FaTensor, v_new: FaTensor, batch: int, block_table: FaTensor,
+                       k_cache: FaTensor, v_cache: FaTensor, page_block_size: int) -> int:
+    """Contract of the paged append only (host code, no GPU needed).  Returns the status."""
+    return load().fa_kv_append_check(_ref(k_new), _ref(v_new), int(batch), _ref(block_table),
+                                     _ref(k_cache), _ref(v_cache), int(page_block_size or 0))
+
+
+def fa_kv_append(k_new: FaTensor, v_new: FaTensor, cu_seqlens_new: int, cu_seqlens_k: int, batch: int,
+                 block_table: FaTensor, k_cache: FaTensor, v_cache: FaTensor, page_block_size: int,
+                 stream: int) -> int:
+    """Raw C-ABI call with descriptors and integer device addresses.  Returns the status."""
+    return load().fa_kv_append(_ref(k_new), _ref(v_new), cu_seqlens_new or None, cu_seqlens_k or None,
+                               int(batch), _ref(block_table), _ref(k_cache), _ref(v_cache),
+                               int(page_block_size or 0), stream or None)
+
+
+def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_cache, v_cache,
+              page_block_size: Optional[int] = None, stream=None):
+    """Write new tokens' K/V rows into a paged cache in place (device tensors).
+
+    k_new/v_new (total_new, Hk, D) bf16; cu_seqlens_new / cu_seqlens_k int32 (batch+1,),
+    the latter counting keys after the append; block_table (batch, max_blocks) int32;
+    k_cache/v_cache (num_blocks, P, Hk, D) bf16.  New token j of sequence b lands at
+    logical key Lk_b - Lnew_b + j.  Enqueues on torch's current stream (or ``stream``).
+    """
+    import torch
+    for name, t in (("cu_seqlens_new", cu_seqlens_new), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+            raise FlashAttnError(7, "%s must be a contiguous 1-d int32 tensor" % name)
+    batch = cu_seqlens_new.shape[0] - 1
+    if cu_seqlens_k.shape[0] != batch + 1:
+        raise FlashAttnError(7, "cu_seqlens_new and cu_seqlens_k must both have batch+1 entries")
+    if page_block_size is None:
+        page_block_size = k_cache.shape[1] if k_cache.dim() == 4 else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(k_cache.device).cuda_stream
+    rc = fa_kv_append(_tdesc(k_new), _tdesc(v_new), cu_seqlens_new.data_ptr(), cu_seqlens_k.data_ptr(),
+                      batch, _tdesc(block_table), _tdesc(k_cache), _tdesc(v_cache), page_block_size,
+                      int(stream))
+    _raise_on(rc)
+    return k_cache, v_cache
 
 
 def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,

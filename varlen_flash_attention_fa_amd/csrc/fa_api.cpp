@@ -157,6 +157,77 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
     return FA_OK;
 }
 
+// Contract of the paged K/V append.  Its page and head-size rules are the ones
+// the pages state for the paged pools the forward reads (pages "paged
+// flash-attn requires page_block_size", "page_block_size ... does not match k
+// shape" and "... to be a multiple of 32"), with the same texts.
+int append_check_impl(const fa_tensor* k_new, const fa_tensor* v_new, int32_t batch, const fa_tensor* bt,
+                      const fa_tensor* k_cache, const fa_tensor* v_cache, int32_t page_block_size) {
+    if (!k_new || !v_new || !k_cache || !v_cache || !bt)
+        return fail(FA_ERR_ARGUMENT, "k_new, v_new, block_table, k_cache and v_cache descriptors must not be NULL");
+    for (const fa_tensor* t : {k_new, v_new, k_cache, v_cache, bt})
+        if (t->rank < 0 || t->rank > 4)
+            return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
+    for (const fa_tensor* t : {k_new, v_new, k_cache, v_cache})
+        if (t->dtype != FA_DTYPE_BF16)
+            return fail(FA_ERR_DTYPE, "kv append takes bf16 k_new/v_new/k_cache/v_cache (dtype code %d)",
+                        (int)t->dtype);
+    if (k_new->rank != 3 || v_new->rank != 3 || k_cache->rank != 4 || v_cache->rank != 4)
+        return fail(FA_ERR_RANK,
+                    "kv append expects k_new/v_new of rank 3 and k_cache/v_cache of rank 4 (got %d, %d, %d, %d)",
+                    (int)k_new->rank, (int)v_new->rank, (int)k_cache->rank, (int)v_cache->rank);
+    if (k_new->stride[2] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of k_new must be contiguous %s", dims(k_new, true).c_str());
+    if (v_new->stride[2] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of v_new must be contiguous %s", dims(v_new, true).c_str());
+    if (k_cache->stride[3] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of k must be contiguous %s", dims(k_cache, true).c_str());
+    if (v_cache->stride[3] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of v must be contiguous %s", dims(v_cache, true).c_str());
+    for (const fa_tensor* t : {k_new, v_new, k_cache, v_cache, bt})
+        for (int i = 0; i < t->rank; ++i)
+            if (t->shape[i] < 0 || t->stride[i] < 0)
+                return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(t, false).c_str(),
+                            dims(t, true).c_str());
+    if (!same_dims(k_cache, v_cache))
+        return fail(FA_ERR_SHAPE, "shape mismatch k %s and v %s", dims(k_cache, false).c_str(),
+                    dims(v_cache, false).c_str());
+    if (!same_dims(k_new, v_new))
+        return fail(FA_ERR_SHAPE, "shape mismatch k_new %s and v_new %s", dims(k_new, false).c_str(),
+                    dims(v_new, false).c_str());
+    if (k_new->shape[1] != k_cache->shape[2] || k_new->shape[2] != k_cache->shape[3])
+        return fail(FA_ERR_SHAPE, "shape mismatch k_new %s and k %s", dims(k_new, false).c_str(),
+                    dims(k_cache, false).c_str());
+    const int64_t page = k_cache->shape[1], head_size = k_cache->shape[3];
+    if (page_block_size <= 0) return fail(FA_ERR_PAGE_SIZE, "paged flash-attn requires page_block_size");
+    if ((int64_t)page_block_size != page)
+        return fail(FA_ERR_PAGE_SIZE, "page_block_size %d does not match k shape %s", (int)page_block_size,
+                    dims(k_cache, false).c_str());
+    if (page % 32 != 0)
+        return fail(FA_ERR_PAGE_SIZE, "paged flash-attn requires page_block_size to be a multiple of 32 (got %lld)",
+                    (long long)page);
+    if (head_size > 512)
+        return fail(FA_ERR_HEAD_DIM, "paged flash-attn supports head sizes up to 512 (got %lld)",
+                    (long long)head_size);
+    if (head_size < 1 || k_new->shape[1] < 1)
+        return fail(FA_ERR_HEAD_DIM, "kv append needs head_dim >= 1 and num_heads_k >= 1 (got %lld, %lld)",
+                    (long long)head_size, (long long)k_new->shape[1]);
+    if (batch < 0) return fail(FA_ERR_ARGUMENT, "batch must be >= 0 (got %d)", (int)batch);
+    if (bt->dtype != FA_DTYPE_I32)
+        return fail(FA_ERR_DTYPE, "block_table must be int32 (dtype code %d)", (int)bt->dtype);
+    if (bt->rank != 2 || bt->shape[0] != batch)
+        return fail(FA_ERR_SHAPE, "block_table must have shape (batch=%d, max_blocks) (got %s)", (int)batch,
+                    dims(bt, false).c_str());
+    if (bt->stride[1] != 1 && bt->shape[1] > 1)
+        return fail(FA_ERR_CONTIGUOUS, "block_table last dimension must be contiguous");
+    if (bt->shape[1] * page >= INT32_MAX)
+        return fail(FA_ERR_ARGUMENT, "max_blocks * page_block_size must be below 2^31");
+    if (k_cache->shape[0] >= INT32_MAX) return fail(FA_ERR_ARGUMENT, "num_blocks must be below 2^31");
+    if (k_new->shape[0] * k_new->shape[1] * head_size >= INT32_MAX)
+        return fail(FA_ERR_ARGUMENT, "total_new * num_heads_k * head_dim must be below 2^31");
+    return FA_OK;
+}
+
 fa::Shapes shapes_of(const fa_tensor* q, const fa_tensor* k, int32_t batch, const fa_tensor* bt,
                      int32_t page_block_size) {
     fa::Shapes s;
@@ -308,6 +379,64 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
 
     rc = fa::launch_fwd(plan, p, stream, g_ev_start, g_ev_stop);
     if (rc) return fail(rc, "kernel launch failed: %s", fa::last_hip_error());
+    return FA_OK;
+}
+
+int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t batch,
+                       const fa_tensor* block_table, const fa_tensor* k_cache, const fa_tensor* v_cache,
+                       int32_t page_block_size) {
+    return append_check_impl(k_new, v_new, batch, block_table, k_cache, v_cache, page_block_size);
+}
+
+int fa_kv_append(const fa_tensor* k_new, const fa_tensor* v_new, const int32_t* cu_seqlens_new,
+                 const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
+                 const fa_tensor* k_cache, const fa_tensor* v_cache, int32_t page_block_size, void* stream) {
+    int rc = append_check_impl(k_new, v_new, batch, block_table, k_cache, v_cache, page_block_size);
+    if (rc) return rc;
+    const int64_t total_new = k_new->shape[0];
+    if (batch == 0 || total_new == 0) return FA_OK;  // nothing to write
+
+    if (!cu_seqlens_new || !is_device_ptr(cu_seqlens_new))
+        return fail(FA_ERR_DEVICE, "seqlens_new must be a cuda tensor");
+    if (!cu_seqlens_k || !is_device_ptr(cu_seqlens_k))
+        return fail(FA_ERR_DEVICE, "seqlens_k must be a cuda tensor");
+    if (!block_table->data || !is_device_ptr(block_table->data))
+        return fail(FA_ERR_DEVICE, "block_table must be a cuda tensor");
+    if (!k_new->data || !is_device_ptr(k_new->data)) return fail(FA_ERR_DEVICE, "k_new must be a cuda tensor");
+    if (!v_new->data || !is_device_ptr(v_new->data)) return fail(FA_ERR_DEVICE, "v_new must be a cuda tensor");
+    if (!k_cache->data || !is_device_ptr(k_cache->data)) return fail(FA_ERR_DEVICE, "k must be a cuda tensor");
+    if (!v_cache->data || !is_device_ptr(v_cache->data)) return fail(FA_ERR_DEVICE, "v must be a cuda tensor");
+
+    fa::AppendParams p;
+    std::memset(&p, 0, sizeof p);
+    p.k_new = static_cast<const uint16_t*>(k_new->data);
+    p.v_new = static_cast<const uint16_t*>(v_new->data);
+    p.k_cache = static_cast<uint16_t*>(k_cache->data);
+    p.v_cache = static_cast<uint16_t*>(v_cache->data);
+    p.cu_new = cu_seqlens_new;
+    p.cu_k = cu_seqlens_k;
+    p.bt = static_cast<const int32_t*>(block_table->data);
+    p.kn_s0 = k_new->stride[0]; p.kn_s1 = k_new->stride[1];
+    p.vn_s0 = v_new->stride[0]; p.vn_s1 = v_new->stride[1];
+    p.kc_s0 = k_cache->stride[0]; p.kc_s1 = k_cache->stride[1]; p.kc_s2 = k_cache->stride[2];
+    p.vc_s0 = v_cache->stride[0]; p.vc_s1 = v_cache->stride[1]; p.vc_s2 = v_cache->stride[2];
+    p.bt_s0 = block_table->stride[0];
+    p.batch = batch;
+    p.Hk = (int32_t)k_new->shape[1];
+    p.D = (int32_t)k_new->shape[2];
+    p.page = page_block_size;
+    p.bt_width = (int32_t)block_table->shape[1];
+    p.num_blocks = (int32_t)k_cache->shape[0];
+    bool vec = (p.D % 8 == 0);
+    for (const fa_tensor* t : {k_new, v_new, k_cache, v_cache}) {
+        vec = vec && aligned16(t->data);
+        for (int i = 0; i + 1 < t->rank; ++i) vec = vec && (t->stride[i] % 8 == 0);
+    }
+    p.vec = vec ? 1 : 0;
+    p.upr = vec ? p.D / 8 : p.D;
+    p.units = (uint32_t)(total_new * p.Hk * p.upr);
+    rc = fa::launch_kv_append(p, stream, g_ev_start, g_ev_stop);
+    if (rc) return fail(rc, "kernel launch failed: %s", fa::last_append_error());
     return FA_OK;
 }
 

@@ -67,9 +67,30 @@ struct Shapes {
     bool paged;
 };
 
+// Paged K/V append: new token rows scattered into pool blocks.  Strides in elements.
+struct AppendParams {
+    const uint16_t* k_new;   // [total_new][Hk][D] bf16 bits (strided tokens/heads)
+    const uint16_t* v_new;
+    uint16_t* k_cache;       // [num_blocks][page][Hk][D]
+    uint16_t* v_cache;
+    const int32_t* cu_new;   // [batch+1]
+    const int32_t* cu_k;     // [batch+1] key counts after the append
+    const int32_t* bt;       // [batch][bt_width]
+    int64_t kn_s0, kn_s1, vn_s0, vn_s1;
+    int64_t kc_s0, kc_s1, kc_s2, vc_s0, vc_s1, vc_s2;
+    int64_t bt_s0;
+    int32_t batch, Hk, D, page, bt_width, num_blocks;
+    int32_t vec;             // 1: a unit is 8 elements (16 bytes); 0: one element
+    int32_t upr;             // units per head row: D/8 or D
+    uint32_t units;          // total_new * Hk * upr (< 2^31)
+};
+
 int make_plan(const Shapes& s, Plan* plan);   // 0 or an fa_status code
 // 0 or FA_ERR_HIP.  ev_start/ev_stop (hipEvent_t or null) bracket the main kernel.
 int launch_fwd(const Plan& plan, const FwdParams& p, void* stream, void* ev_start, void* ev_stop);
 const char* last_hip_error();
+// 0 or FA_ERR_HIP.  ev_start/ev_stop (hipEvent_t or null) bracket the append kernel.
+int launch_kv_append(const AppendParams& p, void* stream, void* ev_start, void* ev_stop);
+const char* last_append_error();
 
 }  // namespace fa

@@ -31,7 +31,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "Workload", "CONFIGS", "make_config", "make_custom", "normal_bf16",
+    "Workload", "CONFIGS", "make_config", "make_custom", "make_append", "append_config", "normal_bf16",
     "lengths_for", "C4_TOTAL",
 ]
 
@@ -268,6 +268,36 @@ def make_custom(lens_q: Sequence[int], lens_k: Sequence[int], num_heads: int, nu
                     cu_seqlens_k=_cu(lens_k), block_table=block_table, page_block_size=page,
                     softmax_scale=_f32(scale), window_left=int(window_left),
                     window_right=int(window_right))
+
+
+def make_append(lens_new: Sequence[int], lens_k: Sequence[int], num_heads_k: int, head_dim: int, *,
+                page: int, seed: int = 0, width: int = 0, spare: float = 0.1):
+    """Inputs of a paged K/V append: a random pool (as ``make_custom`` builds it)
+    plus new rows.  Returns (wl, k_new, v_new, cu_seqlens_new); ``wl.q`` is k_new
+    (its head count is num_heads_k), ``wl.cu_seqlens_k`` counts keys after the append.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    wl = make_custom(lens_new, lens_k, num_heads_k, num_heads_k, head_dim, page=page, width=width,
+                     spare=spare, rng=rng, seed=seed, name="append")
+    v_new = normal_bf16(rng, tuple(wl.q.shape))
+    return wl, wl.q, v_new, wl.cu_seqlens_q
+
+
+def append_config(name: str, seed: Optional[int] = None) -> Workload:
+    """Paged workload whose last ``lens_q[b]`` keys per sequence are the tokens an
+    append writes.  Paged configs are used as they are; the long-prefill config
+    (non-paged) gets a page-64 pool holding its whole sequences (Lq = Lk), and
+    its ``q`` has num_heads_k heads (the new K rows' shape)."""
+    cfg = CONFIGS[name]
+    if cfg["page"] > 0:
+        return make_config(name, seed)
+    seed = DEFAULT_SEEDS[name] if seed is None else seed
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens_q, lens_k = lengths_for(name, rng)
+    wl = make_custom(lens_q, lens_k, cfg["num_heads_k"], cfg["num_heads_k"], cfg["head_dim"], seed=seed,
+                     page=64, rng=rng, name=name + "-paged")
+    wl.extra["desc"] = cfg["desc"].replace("non-paged", "paged (P64)")
+    return wl
 
 
 def make_config(name: str, seed: Optional[int] = None, *, poison: bool = False) -> Workload:
