@@ -126,6 +126,30 @@ def attention_workload(wl, token_sel=None, nthreads=None):
                      token_sel=token_sel, nthreads=nthreads)
 
 
+def attention_padded(q, k, v, softmax_scale: float = 1.0, window_left: int = -1, window_right: int = -1,
+                     nthreads: Optional[int] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """fp64 attention over padded batch-major inputs: every batch element is an
+    independent sequence (the non-varlen FlashAttention the pages point padded
+    callers to), so batch element b is one call of :func:`attention` on q[b],
+    k[b], v[b].
+
+    q: (B, Sq, H, D); k, v: (B, Sk, Hk, D) bf16 (any strides).  Returns ``out``
+    (B, Sq, H, D) float64 and ``lse`` (B, H, Sq) float64 (natural log).
+    """
+    B, Sq, H, D = q.shape
+    Sk = k.shape[1]
+    out = np.zeros((B, Sq, H, D), dtype=np.float64)
+    lse = np.zeros((B, H, Sq), dtype=np.float64)
+    cu_q = np.array([0, Sq], dtype=np.int32)
+    cu_k = np.array([0, Sk], dtype=np.int32)
+    for b in range(B):
+        o, l = attention(q[b], k[b], v[b], cu_q, cu_k, None, 0, softmax_scale, window_left, window_right,
+                         nthreads=nthreads)
+        out[b] = o
+        lse[b] = l
+    return out, lse
+
+
 def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_pool, v_pool, strict=True):
     """Reference paged K/V append; returns new (k_pool, v_pool) uint16 arrays (inputs untouched).
 

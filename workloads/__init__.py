@@ -31,7 +31,8 @@ import numpy as np
 import torch
 
 __all__ = [
-    "Workload", "CONFIGS", "make_config", "make_custom", "make_append", "append_config", "normal_bf16",
+    "Workload", "CONFIGS", "make_config", "make_custom", "make_append", "append_config", "make_padded",
+    "PADDED", "normal_bf16",
     "lengths_for", "C4_TOTAL",
 ]
 
@@ -281,6 +282,35 @@ def make_append(lens_new: Sequence[int], lens_k: Sequence[int], num_heads_k: int
                      spare=spare, rng=rng, seed=seed, name="append")
     v_new = normal_bf16(rng, tuple(wl.q.shape))
     return wl, wl.q, v_new, wl.cu_seqlens_q
+
+
+def make_padded(B: int, Sq: int, Sk: int, num_heads: int, num_heads_k: int, head_dim: int, *,
+                seed: int = 0, layout: str = "bshd"):
+    """Padded inputs q (B, Sq, H, D), k/v (B, Sk, Hk, D) bf16, drawn q, k, v in that
+    order.  ``layout="bhsd"`` draws them head-major, (B, H, S, D) contiguous, and
+    returns (B, S, H, D) views of those (strided, not mergeable into tokens)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    if layout == "bhsd":
+        q = normal_bf16(rng, (B, num_heads, Sq, head_dim)).transpose(1, 2)
+        k = normal_bf16(rng, (B, num_heads_k, Sk, head_dim)).transpose(1, 2)
+        v = normal_bf16(rng, (B, num_heads_k, Sk, head_dim)).transpose(1, 2)
+    else:
+        q = normal_bf16(rng, (B, Sq, num_heads, head_dim))
+        k = normal_bf16(rng, (B, Sk, num_heads_k, head_dim))
+        v = normal_bf16(rng, (B, Sk, num_heads_k, head_dim))
+    return q, k, v
+
+
+# Padded (non-varlen) workloads, batch-major with uniform lengths: the long-prefill
+# batch at a uniform length, and a decode batch at a uniform cache length.
+PADDED = {
+    "p4": dict(desc="padded prefill (8, 8192) H64/Hk8 D128, causal, window_left 4096",
+               B=8, Sq=8192, Sk=8192, num_heads=64, num_heads_k=8, head_dim=128, window_left=4096,
+               window_right=0, seed=1004),
+    "p2": dict(desc="padded decode (64, q 1, kv 4096) H32/Hk8 D128",
+               B=64, Sq=1, Sk=4096, num_heads=32, num_heads_k=8, head_dim=128, window_left=-1,
+               window_right=0, seed=1002),
+}
 
 
 def append_config(name: str, seed: Optional[int] = None) -> Workload:
