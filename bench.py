@@ -22,7 +22,9 @@ bounded sample of the same workload on this host's cores).
 
 ``--op append`` times the paged K/V append instead (``fa_kv_append``): each
 sequence of a paged workload appends as many new tokens as it has query rows
-(its last keys), reported as GB/s of algorithmic HBM traffic.
+(its last keys), reported as GB/s of algorithmic HBM traffic.  ``--op padded``
+times the padded (batch-major) entry ``fa_padded_fwd`` on the padded workloads
+(``--workload p4``: uniform-length long prefill; ``p2``: uniform decode batch).
 """
 from __future__ import annotations
 
@@ -386,6 +388,108 @@ def bench_append(args, fa, W, hip, dev, stream):
     return 0
 
 
+# ------------------------------------------------------------- padded bench
+
+def bench_padded(args, fa, W, hip, dev, stream):
+    import torch
+    cfg = W.PADDED[args.workload]
+    B, Sq, Sk, H, Hk, D = (cfg[x] for x in ("B", "Sq", "Sk", "num_heads", "num_heads_k", "head_dim"))
+    seed = cfg["seed"] if args.seed is None else args.seed
+    print("bench: generating %s (padded)" % args.workload, file=sys.stderr, flush=True)
+    q, k, v = W.make_padded(B, Sq, Sk, H, Hk, D, seed=seed)
+    scale = float(np.float32(1.0 / math.sqrt(D)))
+    # the equivalent varlen description (uniform offsets) gives the algorithmic work
+    # and feeds the oracle's CPU leg
+    wl = W.Workload(name=args.workload, seed=seed, q=q.reshape(B * Sq, H, D), k=k.reshape(B * Sk, Hk, D),
+                    v=v.reshape(B * Sk, Hk, D), cu_seqlens_q=(np.arange(B + 1) * Sq).astype(np.int32),
+                    cu_seqlens_k=(np.arange(B + 1) * Sk).astype(np.int32), block_table=None,
+                    page_block_size=0, softmax_scale=scale, window_left=cfg["window_left"],
+                    window_right=cfg["window_right"])
+    work = work_of(wl)
+    decode = Sq * (H // Hk) <= 64
+    per_copy = (k.numel() + v.numel() + 2 * q.numel()) * 2
+    ncopies = int(min(8, max(1, math.ceil(2.0e9 / per_copy))))
+    with torch.cuda.stream(stream):
+        copies = []
+        for _ in range(ncopies):
+            d = dict(q=q.to(dev), k=k.to(dev), v=v.to(dev))
+            d["out"] = torch.empty_like(d["q"])
+            copies.append(d)
+        torch.cuda.synchronize()
+    calls = [(fa._tdesc(d["q"]), fa._tdesc(d["k"]), fa._tdesc(d["v"]), fa._tdesc(d["out"])) for d in copies]
+    ws_bytes = fa.fa_padded_workspace_bytes(*calls[0][:3])
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+
+    def step(i, ev_k=None):
+        dq, dk, dv, do = calls[i % ncopies]
+        if ev_k is not None:
+            fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
+        rc = fa.fa_padded_fwd(dq, dk, dv, do, scale, cfg["window_left"], cfg["window_right"], 0,
+                              workspace.data_ptr() if ws_bytes else 0, ws_bytes, sh)
+        if rc:
+            raise RuntimeError(fa.fa_last_error())
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    every = max(1, args.event_every)
+    sampled = [i for i in range(K) if i % every == every // 2] or [K // 2]
+    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
+    print("bench: timing %d padded steps (events on %d of them)" % (K, len(sampled)), file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if i in ev_kern:
+            step(i, ev_kern[i])
+            fa.fa_varlen_set_kernel_events(0, 0)
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
+    for a, b in ev_kern.values():
+        hip.destroy(a)
+        hip.destroy(b)
+    kern_mean = float(kern_ms.mean())
+    if decode:
+        value, unit = work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9, "GB/s"
+        achieved = work["total_bytes"] / (kern_mean * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        value, unit = work["flops"] / (ms_per_step * 1e-3) / 1e12, "TFLOP/s"
+        achieved = work["flops"] / (kern_mean * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
+    roof["traffic"] = None
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, work, decode)
+    props = torch.cuda.get_device_properties(dev)
+    line = {
+        "metric": "padded (batch-major) attention: prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)",
+        "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seed %d)" % seed,
+        "config": {"workload": "%s: %s" % (args.workload, cfg["desc"]), "batch": B, "seqlen_q": Sq,
+                   "seqlen_k": Sk, "num_heads": H, "num_heads_k": Hk, "head_dim": D,
+                   "window_left": cfg["window_left"], "window_right": cfg["window_right"],
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "detail": {"main_kernel_ms_mean": round(kern_mean, 5), "event_sampled_steps": len(sampled),
+                   "algorithmic_flop": work["flops"], "algorithmic_total_bytes": work["total_bytes"],
+                   "input_copies_rotated": ncopies, "workspace_bytes": ws_bytes,
+                   "kernel_source_sha256_16": kernel_sha(), "device": props.name},
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ---------------------------------------------------------------------- main
 
 def main(argv=None):
@@ -393,10 +497,12 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5a", "c5b"])
+    ap.add_argument("--workload", default=None,
+                    help="c1..c5b (forward, append; default c2) or p2/p4 (padded; default p4)")
     ap.add_argument("--seed", type=int, default=None)
-    ap.add_argument("--op", default="fwd", choices=["fwd", "append"],
-                    help="fwd: the attention forward (default); append: the paged K/V append")
+    ap.add_argument("--op", default="fwd", choices=["fwd", "append", "padded"],
+                    help="fwd: the attention forward (default); append: the paged K/V append; "
+                         "padded: the batch-major entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--event-every", type=int, default=8, metavar="N",
                     help="bracket the call and its main kernel with HIP events on every N-th timed "
@@ -407,6 +513,11 @@ def main(argv=None):
                                                             "COPY_WRITE_CSV"),
                     help="print the HBM-traffic summary of rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+    if args.workload is None:
+        args.workload = "p4" if args.op == "padded" else "c2"
+    valid = ["p2", "p4"] if args.op == "padded" else ["c1", "c2", "c3", "c4", "c5a", "c5b"]
+    if args.workload not in valid:
+        ap.error("--op %s takes --workload in %s" % (args.op, valid))
     if args.counters_summary:
         print(counters_summary(args.workload, *args.counters_summary, copy_mib=1024, op=args.op), end="")
         return 0
@@ -438,6 +549,8 @@ def main(argv=None):
     hip = Hip()
     if args.op == "append":
         return bench_append(args, fa, W, hip, dev, stream)
+    if args.op == "padded":
+        return bench_padded(args, fa, W, hip, dev, stream)
     print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
     wl = W.make_config(args.workload, args.seed)
     work = work_of(wl)

@@ -4,8 +4,9 @@
  * The forward pass of softmax attention over sequences packed back to back
  * ("varlen"), with grouped-query heads, a softmax scale, a left/right key
  * window around the bottom-right aligned diagonal, and an optional paged K/V
- * cache read through a per-sequence block table; plus the append that writes
- * new tokens' K/V into such a paged cache.
+ * cache read through a per-sequence block table; the same forward over padded
+ * (batch, seqlen, heads, head_dim) tensors; and the append that writes new
+ * tokens' K/V into a paged cache.
  *
  * The operation and its argument contract are those of candle's
  * FlashAttentionVarLen forward (huggingface/candle, candle-flash-attn), as the
@@ -138,6 +139,34 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                   size_t workspace_bytes, void* stream);
 
 /*
+ * Padded (non-varlen) entry: the same forward over batch-major tensors in which
+ * every sequence has the same length, the layout the pages send callers to
+ * when they hold (B, S, H, D) tensors instead of packed ones (page
+ * "flash-attn-varlen expects input tensors of rank 3", Solutions and When it
+ * happens: padded batch attention goes to the non-varlen FlashAttention).  It
+ * computes exactly what fa_varlen_fwd computes with cu_seqlens_q = b * Sq and
+ * cu_seqlens_k = b * Sk (no cu arrays are needed).
+ *
+ *   q, out   (B, Sq, H, D) bf16, last dim contiguous, any other strides
+ *            (for instance a (B, H, S, D) tensor viewed as (B, S, H, D)).
+ *   k, v     (B, Sk, Hk, D) bf16, last dim contiguous, same shape; H % Hk == 0;
+ *            1 <= D <= 512; B*Sq*H and B*Sk below 2^31.
+ *   softmax_scale, window_left, window_right  as for fa_varlen_fwd (query row i
+ *            sits at key position i + Sk - Sq).
+ *   softmax_lse  NULL or device fp32 (B, H, Sq), natural log.
+ *   workspace    at least fa_padded_workspace_bytes() bytes (may be NULL if 0).
+ * Errors, ownership and asynchrony as for fa_varlen_fwd; fa_padded_check runs
+ * the contract alone without a GPU.
+ */
+int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out);
+
+int fa_padded_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, size_t* bytes);
+
+int fa_padded_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                  float softmax_scale, int32_t window_left, int32_t window_right, float* softmax_lse,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * fa_kv_append_check -- the contract of fa_kv_append alone (host code, no GPU
  * needed, no pointer dereferenced).  Returns FA_OK or the first failing check.
  */
@@ -181,9 +210,9 @@ int fa_kv_append(const fa_tensor* k_new, const fa_tensor* v_new, const int32_t* 
 /*
  * fa_varlen_set_kernel_events -- measurement hook for benchmarks.  With both
  * arguments non-NULL (hipEvent_t handles created by the caller), every later
- * fa_varlen_fwd (fa_kv_append) on this thread records `start_event`
- * immediately before and `stop_event` immediately after its main attention
- * kernel (its append kernel), on the call's stream, so the caller can read
+ * fa_varlen_fwd / fa_padded_fwd (fa_kv_append) on this thread records
+ * `start_event` immediately before and `stop_event` immediately after its main
+ * attention kernel (its append kernel), on the call's stream, so the caller can read
  * that kernel's duration with hipEventElapsedTime.  NULL, NULL turns it off.  The events stay owned by the
  * caller.  Always returns FA_OK.
  */

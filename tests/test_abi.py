@@ -298,3 +298,44 @@ def test_append_empty_call_needs_no_gpu(lib):
     """batch 0 or no new tokens: nothing is launched, no device pointer is inspected."""
     assert fa.fa_kv_append(desc([0, 2, 64]), desc([0, 2, 64]), 0, 0, 3, BT3, KC, KC, 32, 0) == 0
     assert fa.fa_kv_append(KN, KN, 0, 0, 0, desc([0, 4], dtype=FA_DTYPE_I32), KC, KC, 32, 0) == 0
+
+
+# ------------------------------------------------------------ padded entry
+
+QP = desc([2, 5, 4, 64])
+KP4 = desc([2, 9, 2, 64])
+
+
+def pcheck(q=QP, k=KP4, v=KP4, out=None):
+    rc = fa.fa_padded_check(q, k, v, out)
+    return rc, fa.fa_last_error() if rc else ""
+
+
+def test_padded_contract(lib):
+    code = {v: k for k, v in fa.STATUS.items()}
+    assert pcheck() == (0, "")
+    assert pcheck(out=QP)[0] == 0
+    # head-major views are accepted
+    assert pcheck(q=desc([2, 5, 4, 64], stride=[1280, 64, 320, 1]))[0] == 0
+    assert pcheck(q=desc([10, 4, 64]))[0] == code["FA_ERR_RANK"]
+    assert pcheck(k=desc([2, 9, 2, 64], dtype=FA_DTYPE_I32))[0] == code["FA_ERR_DTYPE"]
+    c, t, _ = tmpl("the last dim of q must")
+    rc, msg = pcheck(q=desc([2, 5, 4, 64], stride=[2560, 512, 128, 2]))
+    assert rc == c and msg == render(t, q_stride=dl([2560, 512, 128, 2]))
+    c, t, _ = tmpl("shape mismatch k {:?} and v")
+    rc, msg = pcheck(v=desc([2, 8, 2, 64]))
+    assert rc == c and msg == render(t, _seq=[dl([2, 9, 2, 64]), dl([2, 8, 2, 64])])
+    assert pcheck(k=desc([3, 9, 2, 64]), v=desc([3, 9, 2, 64]))[0] == code["FA_ERR_SHAPE"]
+    assert pcheck(k=desc([2, 9, 3, 64]), v=desc([2, 9, 3, 64]))[0] == code["FA_ERR_ARGUMENT"]
+    assert pcheck(q=desc([2, 5, 4, 520]), k=desc([2, 9, 2, 520]), v=desc([2, 9, 2, 520]))[0] == code["FA_ERR_HEAD_DIM"]
+    assert pcheck(out=desc([2, 5, 4, 32]))[0] == code["FA_ERR_SHAPE"]
+
+
+def test_padded_workspace_and_empty_call(lib):
+    assert fa.fa_padded_workspace_bytes(QP, KP4, KP4) > 0
+    # decode-shaped calls split keys: partials make the workspace larger
+    big = fa.fa_padded_workspace_bytes(desc([64, 1, 32, 128]), desc([64, 4096, 8, 128]), desc([64, 4096, 8, 128]))
+    assert big > 64 * 32 * 128 * 4
+    # no batch or no query: nothing is launched, no pointer is inspected
+    assert fa.fa_padded_fwd(desc([0, 5, 4, 64]), desc([0, 9, 2, 64]), desc([0, 9, 2, 64]),
+                            desc([0, 5, 4, 64]), 0.1, -1, 0, 0, 0, 0, 0) == 0

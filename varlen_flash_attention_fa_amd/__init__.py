@@ -6,8 +6,9 @@ device memory and the current stream.  There is no CPU fallback: if the shared
 library has not been built, importing the low-level functions raises.
 
 Low-level names mirror the C ABI (``fa_varlen_check``, ``fa_varlen_workspace_bytes``,
-``fa_varlen_fwd``, ``fa_kv_append_check``, ``fa_kv_append``, ``fa_last_error``) and
-take :class:`FaTensor` descriptors; :func:`varlen_fwd` and :func:`kv_append` are the
+``fa_varlen_fwd``, ``fa_padded_check``, ``fa_padded_workspace_bytes``, ``fa_padded_fwd``,
+``fa_kv_append_check``, ``fa_kv_append``, ``fa_last_error``) and take :class:`FaTensor`
+descriptors; :func:`varlen_fwd`, :func:`padded_fwd` and :func:`kv_append` are the
 tensor-level convenience wrappers.
 """
 from __future__ import annotations
@@ -21,6 +22,7 @@ __all__ = [
     "FaTensor", "FlashAttnError", "lib_path", "load", "fa_varlen_check",
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
     "fa_varlen_set_kernel_events", "fa_kv_append_check", "fa_kv_append", "kv_append",
+    "fa_padded_check", "fa_padded_workspace_bytes", "fa_padded_fwd", "padded_fwd",
     "FA_DTYPE_BF16", "FA_DTYPE_I32", "STATUS",
 ]
 
@@ -76,6 +78,13 @@ def load():
     lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_varlen_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_varlen_set_kernel_events.restype = ctypes.c_int
+    lib.fa_padded_check.argtypes = [P, P, P, P]
+    lib.fa_padded_check.restype = ctypes.c_int
+    lib.fa_padded_workspace_bytes.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_size_t)]
+    lib.fa_padded_workspace_bytes.restype = ctypes.c_int
+    lib.fa_padded_fwd.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_padded_fwd.restype = ctypes.c_int
     lib.fa_kv_append_check.argtypes = [P, P, ctypes.c_int32, P, P, P, ctypes.c_int32]
     lib.fa_kv_append_check.restype = ctypes.c_int
     lib.fa_kv_append.argtypes = [P, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, P, P, P,
@@ -156,6 +165,55 @@ def fa_varlen_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqle
 def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:
     """Measurement hook: bracket the main kernel of later calls with these hipEvent_t handles."""
     return load().fa_varlen_set_kernel_events(start_event or None, stop_event or None)
+
+
+def fa_padded_check(q: FaTensor, k: FaTensor, v: FaTensor, out: Optional[FaTensor]) -> int:
+    """Contract of the padded entry only (host code, no GPU needed).  Returns the status."""
+    return load().fa_padded_check(_ref(q), _ref(k), _ref(v), _ref(out))
+
+
+def fa_padded_workspace_bytes(q: FaTensor, k: FaTensor, v: FaTensor) -> int:
+    n = ctypes.c_size_t(0)
+    _raise_on(load().fa_padded_workspace_bytes(_ref(q), _ref(k), _ref(v), ctypes.byref(n)))
+    return int(n.value)
+
+
+def fa_padded_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, softmax_scale: float,
+                  window_left: int, window_right: int, softmax_lse: int, workspace: int,
+                  workspace_bytes: int, stream: int) -> int:
+    """Raw C-ABI call of the padded entry.  Returns the status."""
+    return load().fa_padded_fwd(_ref(q), _ref(k), _ref(v), _ref(out), float(softmax_scale), int(window_left),
+                                int(window_right), softmax_lse or None, workspace or None,
+                                int(workspace_bytes), stream or None)
+
+
+def padded_fwd(q, k, v, softmax_scale: Optional[float] = None, window_left: int = -1,
+               window_right: int = -1, return_lse: bool = False, out=None, workspace=None, stream=None):
+    """Forward over padded (B, Sq, H, D) / (B, Sk, Hk, D) device tensors.
+
+    Returns ``out`` (B, Sq, H, D) bf16, plus ``lse`` (B, H, Sq) fp32 if ``return_lse``.
+    """
+    import torch
+    if softmax_scale is None:
+        softmax_scale = 1.0 / math.sqrt(q.shape[-1])
+    dq, dk, dv = _tdesc(q), _tdesc(k), _tdesc(v)
+    if out is None:
+        out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    dout = _tdesc(out)
+    _raise_on(fa_padded_check(dq, dk, dv, dout))
+    nbytes = fa_padded_workspace_bytes(dq, dk, dv)
+    if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    lse = None
+    if return_lse:
+        lse = torch.empty((q.shape[0], q.shape[2], q.shape[1]), dtype=torch.float32, device=q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+    _raise_on(fa_padded_fwd(dq, dk, dv, dout, softmax_scale, window_left, window_right,
+                            lse.data_ptr() if lse is not None else 0,
+                            workspace.data_ptr() if (nbytes and workspace is not None) else 0, nbytes,
+                            int(stream)))
+    return (out, lse) if return_lse else out
 
 
 def fa_kv_append_check(k_new: FaTensor, v_new: FaTensor, batch: int, block_table: FaTensor,

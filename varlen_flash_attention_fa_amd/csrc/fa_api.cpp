@@ -252,54 +252,101 @@ bool is_device_ptr(const void* p) {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
-}  // namespace
+// Launch-time values that differ between the varlen and the padded entry.
+struct Extra {
+    int32_t padded = 0, uniform_q = 0, uniform_k = 0;
+    int64_t q_bx = 0, k_bx = 0, v_bx = 0, o_bx = 0;
+    int64_t lse_sh = 0, lse_bx = 0;
+    bool vec_ok = true;   // alignment of the strides the 3-d views do not show
+    fa::Shapes shapes{};
+};
 
-extern "C" {
-
-int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-                    int32_t batch, const fa_tensor* block_table, int32_t page_block_size) {
-    return check_impl(q, k, v, out, batch, block_table, page_block_size);
-}
-
-int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, int32_t batch,
-                              const fa_tensor* block_table, int32_t page_block_size, size_t* bytes) {
-    if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
-    int rc = check_impl(q, k, v, nullptr, batch, block_table, page_block_size);
-    if (rc) return rc;
-    fa::Plan plan;
-    rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
-    if (rc) return fail(rc, "no launch plan for these shapes");
-    *bytes = plan.ws_bytes;
+// Contract of the padded (non-varlen) entry: q/out (B, Sq, H, D), k/v (B, Sk, Hk, D).
+int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out) {
+    if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
+    for (const fa_tensor* t : {q, k, v})
+        if (t->rank < 0 || t->rank > 4)
+            return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
+    if (q->dtype != FA_DTYPE_BF16 || k->dtype != FA_DTYPE_BF16 || v->dtype != FA_DTYPE_BF16)
+        return fail(FA_ERR_DTYPE, "flash-attn takes bf16 q/k/v (dtype codes q: %d, k: %d, v: %d)", (int)q->dtype,
+                    (int)k->dtype, (int)v->dtype);
+    if (q->rank != 4 || k->rank != 4 || v->rank != 4)
+        return fail(FA_ERR_RANK, "flash-attn expects (batch, seqlen, heads, head_dim) tensors of rank 4 (q: %d, k: %d, v: %d)",
+                    (int)q->rank, (int)k->rank, (int)v->rank);
+    if (q->stride[3] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of q must be contiguous %s", dims(q, true).c_str());
+    if (k->stride[3] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of k must be contiguous %s", dims(k, true).c_str());
+    if (v->stride[3] != 1)
+        return fail(FA_ERR_CONTIGUOUS, "the last dim of v must be contiguous %s", dims(v, true).c_str());
+    for (const fa_tensor* t : {q, k, v})
+        for (int i = 0; i < 4; ++i)
+            if (t->shape[i] < 0 || t->stride[i] < 0)
+                return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(t, false).c_str(),
+                            dims(t, true).c_str());
+    if (!same_dims(k, v))
+        return fail(FA_ERR_SHAPE, "shape mismatch k %s and v %s", dims(k, false).c_str(), dims(v, false).c_str());
+    if (k->shape[0] != q->shape[0] || k->shape[3] != q->shape[3])
+        return fail(FA_ERR_SHAPE, "shape mismatch q %s and k %s", dims(q, false).c_str(), dims(k, false).c_str());
+    const int64_t B = q->shape[0], Sq = q->shape[1], H = q->shape[2], D = q->shape[3];
+    const int64_t Sk = k->shape[1], Hk = k->shape[2];
+    if (D < 1 || D > 512)
+        return fail(FA_ERR_HEAD_DIM, "flash-attn supports head sizes 1..512 (got %lld)", (long long)D);
+    if (H < 1 || Hk < 1 || H % Hk != 0)
+        return fail(FA_ERR_ARGUMENT,
+                    "number of heads in q (%lld) must be a positive multiple of the number of heads in k/v (%lld)",
+                    (long long)H, (long long)Hk);
+    if (B * Sq * H >= INT32_MAX || B * Sk >= INT32_MAX || B >= INT32_MAX)
+        return fail(FA_ERR_ARGUMENT, "batch * seqlen_q * heads and batch * seqlen_k must be below 2^31");
+    if (out) {
+        if (out->dtype != FA_DTYPE_BF16) return fail(FA_ERR_DTYPE, "out must be bf16 (dtype code %d)", (int)out->dtype);
+        if (!same_dims(out, q))
+            return fail(FA_ERR_SHAPE, "out must have the shape of q %s (got %s)", dims(q, false).c_str(),
+                        dims(out, false).c_str());
+        if (out->stride[3] != 1)
+            return fail(FA_ERR_CONTIGUOUS, "the last dim of out must be contiguous %s", dims(out, true).c_str());
+        for (int i = 0; i < 4; ++i)
+            if (out->stride[i] < 0)
+                return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(out, false).c_str(),
+                            dims(out, true).c_str());
+    }
     return FA_OK;
 }
 
-int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
-                  const fa_tensor* block_table, int32_t page_block_size, float softmax_scale,
-                  int32_t window_left, int32_t window_right, float* softmax_lse, void* workspace,
-                  size_t workspace_bytes, void* stream) {
-    if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
-    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size);
-    if (rc) return rc;
+fa::Shapes padded_shapes(const fa_tensor* q, const fa_tensor* k) {
+    fa::Shapes s;
+    s.total_q = q->shape[0] * q->shape[1];
+    s.H = q->shape[2];
+    s.D = q->shape[3];
+    s.Hk = k->shape[2];
+    s.max_lk = k->shape[1];  // every sequence has seqlen_k keys
+    s.batch = q->shape[0];
+    s.paged = false;
+    return s;
+}
+
+// Device checks, plan, parameters and launch shared by both entries.  q/k/v/out
+// are rank-3 (token, head, dim) views (paged k/v: rank 4); cu arrays are only
+// read when the call is varlen.
+int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
+            int32_t page_block_size, float softmax_scale, int32_t window_left, int32_t window_right,
+            float* softmax_lse, void* workspace, size_t workspace_bytes, void* stream, const Extra& ex) {
     const bool paged = block_table != nullptr;
     const int64_t total_q = q->shape[0];
-    if (batch == 0 || total_q == 0) return FA_OK;  // nothing to compute, nothing written
-
-    if (!cu_seqlens_q || !is_device_ptr(cu_seqlens_q))
-        return fail(FA_ERR_DEVICE, "seqlens_q must be a cuda tensor");
-    if (!cu_seqlens_k || !is_device_ptr(cu_seqlens_k))
-        return fail(FA_ERR_DEVICE, "seqlens_k must be a cuda tensor");
     if (paged && (!block_table->data || !is_device_ptr(block_table->data)))
         return fail(FA_ERR_DEVICE, "block_table must be a cuda tensor");
     if (!q->data || !is_device_ptr(q->data)) return fail(FA_ERR_DEVICE, "q must be a cuda tensor");
-    if (!k->data || !is_device_ptr(k->data)) return fail(FA_ERR_DEVICE, "k must be a cuda tensor");
-    if (!v->data || !is_device_ptr(v->data)) return fail(FA_ERR_DEVICE, "v must be a cuda tensor");
+    // k/v without any row are never read (every sequence then has no key)
+    const bool kv_empty = k->shape[0] == 0;
+    if (!kv_empty && (!k->data || !is_device_ptr(k->data))) return fail(FA_ERR_DEVICE, "k must be a cuda tensor");
+    if (!kv_empty && (!v->data || !is_device_ptr(v->data))) return fail(FA_ERR_DEVICE, "v must be a cuda tensor");
     if (!out->data || !is_device_ptr(out->data)) return fail(FA_ERR_DEVICE, "out must be a cuda tensor");
     if (softmax_lse && !is_device_ptr(softmax_lse))
         return fail(FA_ERR_DEVICE, "softmax_lse must be a cuda tensor");
 
     fa::Plan plan;
-    rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
+    int rc = fa::make_plan(ex.shapes, &plan);
     if (rc) return fail(rc, "no launch plan for these shapes");
     if (plan.ws_bytes) {
         if (!workspace || workspace_bytes < plan.ws_bytes)
@@ -347,6 +394,15 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     p.chunk = plan.chunk;
     p.max_chunks = plan.max_chunks;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.padded = ex.padded;
+    p.uniform_q = ex.uniform_q;
+    p.uniform_k = ex.uniform_k;
+    p.q_bx = ex.q_bx;
+    p.k_bx = ex.k_bx;
+    p.v_bx = ex.v_bx;
+    p.o_bx = ex.o_bx;
+    p.lse_sh = ex.lse_sh;
+    p.lse_bx = ex.lse_bx;
     {
         unsigned char* ws = static_cast<unsigned char*>(workspace);
         if (plan.max_chunks > 1) {
@@ -360,8 +416,9 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
         p.tok_nc = reinterpret_cast<int32_t*>(ws + plan.off_tok);
     }
     // 16-byte vector access is legal when every row start is 16-byte aligned
-    bool vec = (p.D % 8 == 0);
+    bool vec = (p.D % 8 == 0) && ex.vec_ok;
     for (const fa_tensor* t : {q, k, v, out}) {
+        if (t->shape[0] == 0) continue;  // never read
         vec = vec && aligned16(t->data);
         for (int i = 0; i + 1 < t->rank; ++i) vec = vec && (t->stride[i] % 8 == 0);
     }
@@ -380,6 +437,105 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     rc = fa::launch_fwd(plan, p, stream, g_ev_start, g_ev_stop);
     if (rc) return fail(rc, "kernel launch failed: %s", fa::last_hip_error());
     return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                    int32_t batch, const fa_tensor* block_table, int32_t page_block_size) {
+    return check_impl(q, k, v, out, batch, block_table, page_block_size);
+}
+
+int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, int32_t batch,
+                              const fa_tensor* block_table, int32_t page_block_size, size_t* bytes) {
+    if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
+    int rc = check_impl(q, k, v, nullptr, batch, block_table, page_block_size);
+    if (rc) return rc;
+    fa::Plan plan;
+    rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
+    if (rc) return fail(rc, "no launch plan for these shapes");
+    *bytes = plan.ws_bytes;
+    return FA_OK;
+}
+
+int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                  const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                  const fa_tensor* block_table, int32_t page_block_size, float softmax_scale,
+                  int32_t window_left, int32_t window_right, float* softmax_lse, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+    if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
+    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size);
+    if (rc) return rc;
+    if (batch == 0 || q->shape[0] == 0) return FA_OK;  // nothing to compute, nothing written
+    if (!cu_seqlens_q || !is_device_ptr(cu_seqlens_q))
+        return fail(FA_ERR_DEVICE, "seqlens_q must be a cuda tensor");
+    if (!cu_seqlens_k || !is_device_ptr(cu_seqlens_k))
+        return fail(FA_ERR_DEVICE, "seqlens_k must be a cuda tensor");
+    Extra ex;
+    ex.lse_sh = q->shape[0];
+    ex.shapes = shapes_of(q, k, batch, block_table, page_block_size);
+    return run_fwd(q, k, v, out, cu_seqlens_q, cu_seqlens_k, batch, block_table, page_block_size, softmax_scale,
+                   window_left, window_right, softmax_lse, workspace, workspace_bytes, stream, ex);
+}
+
+int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out) {
+    return padded_check_impl(q, k, v, out);
+}
+
+int fa_padded_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, size_t* bytes) {
+    if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
+    int rc = padded_check_impl(q, k, v, nullptr);
+    if (rc) return rc;
+    fa::Plan plan;
+    rc = fa::make_plan(padded_shapes(q, k), &plan);
+    if (rc) return fail(rc, "no launch plan for these shapes");
+    *bytes = plan.ws_bytes;
+    return FA_OK;
+}
+
+int fa_padded_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                  float softmax_scale, int32_t window_left, int32_t window_right, float* softmax_lse,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
+    int rc = padded_check_impl(q, k, v, out);
+    if (rc) return rc;
+    const int64_t B = q->shape[0], Sq = q->shape[1], Sk = k->shape[1];
+    if (B == 0 || Sq == 0) return FA_OK;
+    // the same operation over (B*S, heads, head_dim) views: row t of sequence b
+    // sits at t * token_stride + b * (batch_stride - S * token_stride)
+    fa_tensor q3, k3, v3, o3;
+    auto flat = [](const fa_tensor* t4, fa_tensor* t3) {
+        *t3 = *t4;
+        t3->rank = 3;
+        t3->shape[0] = t4->shape[0] * t4->shape[1];
+        t3->shape[1] = t4->shape[2];
+        t3->shape[2] = t4->shape[3];
+        t3->stride[0] = t4->stride[1];
+        t3->stride[1] = t4->stride[2];
+        t3->stride[2] = t4->stride[3];
+        t3->shape[3] = t3->stride[3] = 0;
+    };
+    flat(q, &q3);
+    flat(k, &k3);
+    flat(v, &v3);
+    flat(out, &o3);
+    Extra ex;
+    ex.padded = 1;
+    ex.uniform_q = (int32_t)Sq;
+    ex.uniform_k = (int32_t)Sk;
+    ex.q_bx = q->stride[0] - Sq * q->stride[1];
+    ex.k_bx = k->stride[0] - Sk * k->stride[1];
+    ex.v_bx = v->stride[0] - Sk * v->stride[1];
+    ex.o_bx = out->stride[0] - Sq * out->stride[1];
+    ex.lse_sh = Sq;                           // softmax_lse is (B, H, Sq)
+    ex.lse_bx = (q->shape[2] - 1) * Sq;
+    ex.vec_ok = q->stride[0] % 8 == 0 && k->stride[0] % 8 == 0 && v->stride[0] % 8 == 0 &&
+                out->stride[0] % 8 == 0;
+    ex.shapes = padded_shapes(q, k);
+    return run_fwd(&q3, &k3, &v3, &o3, nullptr, nullptr, (int32_t)B, nullptr, 0, softmax_scale, window_left,
+                   window_right, softmax_lse, workspace, workspace_bytes, stream, ex);
 }
 
 int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t batch,

@@ -177,12 +177,16 @@ struct SeqSpan {
 
 __device__ __forceinline__ SeqSpan seq_span(const FwdParams& p, int b) {
     SeqSpan s;
-    const int q0 = min(max(p.cu_q[b], 0), p.total_q);
-    const int q1 = min(max(p.cu_q[b + 1], q0), p.total_q);
+    const bool uq = p.padded != 0;
+    const int cq0 = uq ? b * p.uniform_q : p.cu_q[b];
+    const int cq1 = uq ? cq0 + p.uniform_q : p.cu_q[b + 1];
+    const int q0 = min(max(cq0, 0), p.total_q);
+    const int q1 = min(max(cq1, q0), p.total_q);
     s.q0 = q0;
     s.Lq = q1 - q0;
-    const int k0 = p.cu_k[b];
-    int lk = max(0, p.cu_k[b + 1] - k0);
+    const bool uk = p.padded != 0;
+    const int k0 = uk ? b * p.uniform_k : p.cu_k[b];
+    int lk = max(0, (uk ? k0 + p.uniform_k : p.cu_k[b + 1]) - k0);
     if (p.bt) {
         s.k0 = 0;
         lk = p.num_blocks > 0 ? min(lk, p.max_lk) : 0;
@@ -386,6 +390,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     const int Lq = it.Lq, Lk = it.Lk;
     const int nrows = Lq * p.G;
     const int32_t* bt_row = paged ? p.bt + (int64_t)it.b * p.bt_s0 : nullptr;
+    // extra per-sequence offsets of padded (B, S, ...) k/v (zero for varlen)
+    const int64_t kbx = (int64_t)it.b * p.k_bx, vbx = (int64_t)it.b * p.v_bx;
 
     // keys of this item: union of the tile rows' windows, cut to the chunk
     const int r_first = it.rt * R;
@@ -429,7 +435,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     if (c2 == 0.f) { qzero = true; c2 = 1.f; }
     u32x4 qreg[NKS];
     {
-        const uint16_t* qrow = p.q + (int64_t)(it.q0 + qi) * p.q_s0 + (int64_t)h * p.q_s1;
+        const uint16_t* qrow = p.q + (int64_t)(it.q0 + qi) * p.q_s0 + (int64_t)it.b * p.q_bx + (int64_t)h * p.q_s1;
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
             u32x4 x = (row_ok && !qzero) ? load8(qrow, s * M::KSTEP + kgrp * 8, D, vec) : u32x4{0u, 0u, 0u, 0u};
@@ -505,8 +511,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                     vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg1 * p.v_s0 + (int64_t)hk * p.v_s2);
                     slot0 = ts - base0;
                 } else {
-                    kp0 = kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)(it.k0 + ts) * p.k_s0 + (int64_t)hk * p.k_s1);
-                    vp0 = vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)(it.k0 + ts) * p.v_s0 + (int64_t)hk * p.v_s1);
+                    kp0 = kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)(it.k0 + ts) * p.k_s0 + kbx + (int64_t)hk * p.k_s1);
+                    vp0 = vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)(it.k0 + ts) * p.v_s0 + vbx + (int64_t)hk * p.v_s1);
                 }
                 const int wv = __builtin_amdgcn_readfirstlane(wave);  // lets the compiler keep bases scalar
 #pragma unroll
@@ -536,8 +542,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                         offk = (int64_t)blk * p.k_s0 + (int64_t)slot * p.k_s1 + (int64_t)hk * p.k_s2;
                         offv = (int64_t)blk * p.v_s0 + (int64_t)slot * p.v_s1 + (int64_t)hk * p.v_s2;
                     } else {
-                        offk = (int64_t)(it.k0 + n) * p.k_s0 + (int64_t)hk * p.k_s1;
-                        offv = (int64_t)(it.k0 + n) * p.v_s0 + (int64_t)hk * p.v_s1;
+                        offk = (int64_t)(it.k0 + n) * p.k_s0 + kbx + (int64_t)hk * p.k_s1;
+                        offv = (int64_t)(it.k0 + n) * p.v_s0 + vbx + (int64_t)hk * p.v_s1;
                     }
                     int ck = lpos ^ (rr & SWK);
                     int cv = lpos ^ ((2 * rr) & SWV);
@@ -563,8 +569,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                         rowk = p.k + (int64_t)blk * p.k_s0 + (int64_t)slot * p.k_s1 + (int64_t)hk * p.k_s2;
                         rowv = p.v + (int64_t)blk * p.v_s0 + (int64_t)slot * p.v_s1 + (int64_t)hk * p.v_s2;
                     } else {
-                        rowk = p.k + (int64_t)(it.k0 + nc) * p.k_s0 + (int64_t)hk * p.k_s1;
-                        rowv = p.v + (int64_t)(it.k0 + nc) * p.v_s0 + (int64_t)hk * p.v_s1;
+                        rowk = p.k + (int64_t)(it.k0 + nc) * p.k_s0 + kbx + (int64_t)hk * p.k_s1;
+                        rowv = p.v + (int64_t)(it.k0 + nc) * p.v_s0 + vbx + (int64_t)hk * p.v_s1;
                     }
                     const int ck = lpos ^ (rr & SWK);
                     const int cv = lpos ^ ((2 * rr) & SWV);
@@ -772,7 +778,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             if (kgrp == 0) p.part_lse[((int64_t)it.c * p.total_q + tq) * p.H + h] = lse2;
         }
     } else if (row_ok) {
-        uint16_t* orow = p.out + (int64_t)tq * p.o_s0 + (int64_t)h * p.o_s1;
+        uint16_t* orow = p.out + (int64_t)tq * p.o_s0 + (int64_t)it.b * p.o_bx + (int64_t)h * p.o_s1;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -792,7 +798,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                         if (d + j < D) orow[d + j] = to_bf16(xs[j]);
                 }
             }
-        if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.total_q + tq] = lse2 * 0.6931471805599453f;
+        if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.lse_sh + tq + (int64_t)it.b * p.lse_bx] = lse2 * 0.6931471805599453f;
     }
 }
 
@@ -807,15 +813,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     if (nc <= 1) return;
     const float* pl = p.part_lse + (int64_t)t * p.H + h;
     const int64_t cstride_l = (int64_t)p.total_q * p.H;
+    const int64_t b = p.padded ? t / p.uniform_q : 0;  // only padded calls have per-sequence offsets
+    float* lse = p.lse ? p.lse + (int64_t)h * p.lse_sh + t + b * p.lse_bx : nullptr;
     float M = kNegInf;
     for (int c = lane; c < nc; c += 64) M = fmaxf(M, pl[c * cstride_l]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    uint16_t* orow = p.out + (int64_t)t * p.o_s0 + (int64_t)h * p.o_s1;
+    uint16_t* orow = p.out + (int64_t)t * p.o_s0 + b * p.o_bx + (int64_t)h * p.o_s1;
     const int D = p.D;
     if (M == kNegInf) {  // no chunk saw a key
         for (int d = lane; d < D; d += 64) orow[d] = 0;
-        if (p.lse && lane == 0) p.lse[(int64_t)h * p.total_q + t] = kNegInf;
+        if (lse && lane == 0) *lse = kNegInf;
         return;
     }
     constexpr int PER = DP / 64;
@@ -838,8 +846,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
         const int d = j * 64 + lane;
         if (d < D) orow[d] = to_bf16(acc[j] * inv);
     }
-    if (p.lse && lane == 0)
-        p.lse[(int64_t)h * p.total_q + t] = (M + __builtin_amdgcn_logf(wsum)) * 0.6931471805599453f;
+    if (lse && lane == 0) *lse = (M + __builtin_amdgcn_logf(wsum)) * 0.6931471805599453f;
 }
 
 hipError_t g_last = hipSuccess;

@@ -41,6 +41,15 @@ struct FwdParams {
     int32_t fast_copy;      // 1 = interior K/V tiles may use uniform-base + lane-offset copies
     int32_t k_rowb, v_rowb; // bytes between consecutive key rows (paged: slot stride; packed: token stride)
     float scale_log2;       // softmax_scale * log2(e)
+    // Padded (B, S, H, D) calls: every sequence has uniform_q queries and
+    // uniform_k keys (the offsets are b * uniform_*; no cu_seqlens arrays), and
+    // row t of sequence b sits at t * s0 + b * *_bx, the extra per-sequence
+    // offset of a batch stride that is not S * s0.  Varlen calls: all zero.
+    int32_t padded, uniform_q, uniform_k;
+    int64_t q_bx, k_bx, v_bx, o_bx;
+    // lse element of (token t of sequence b, head h): h * lse_sh + t + b * lse_bx
+    // (varlen: lse_sh = total_q, lse_bx = 0; padded (B, H, Sq): Sq and (H - 1) * Sq)
+    int64_t lse_sh, lse_bx;
 };
 
 enum Kind { KIND_PREFILL = 0, KIND_DECODE = 1 };
