@@ -168,6 +168,11 @@ __device__ __forceinline__ int opaque_lane() {
     return l;
 }  // block-table entries staged in LDS per segment
 
+// Row order of the K operand of the 32x32 S^T product: lane row rho holds key
+// kappa(rho) (bits 2 and 3 swapped), so the 8 keys a lane holds in its score
+// registers are the 8 it supplies as the B operand of O^T = V^T P^T.
+__device__ __forceinline__ int kappa32(int rl) { return (rl & ~12) | ((rl & 4) << 1) | ((rl & 8) >> 1); }
+
 // Sequence b's query rows [q0, q0+Lq) and key count Lk, clamped to the
 // tensors the call was given: cu_seqlens contents are not validated, and a bad
 // table must not make any kernel address outside q/out, k/v or the block table.
@@ -355,6 +360,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     constexpr int SWK = (CH < 16 ? CH : 16) - 1;
     constexpr int SWV = (CH < 16 ? CH : 16) - 1;
     constexpr int RPI = 64 / CH > 0 ? 64 / CH : 1;   // rows per 64-lane copy
+    constexpr int CPD = MR / 8;           // 16-byte chunks per d-block of the PV product
+    constexpr int NPAT = (NDB < (SWV + 1) / CPD) ? NDB : (SWV + 1) / CPD;  // V read XOR patterns
     static_assert(BN % 32 == 0 && (BN * CH) % NT == 0 && CH <= 64 && 64 % CH == 0, "tile shape");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * 2 * TILEB];
@@ -362,7 +369,16 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int hk = blockIdx.y;
+    // Workgroups are dispatched round-robin over the 8 XCDs (each with its own
+    // L2).  Work units (item, K/V head) are numbered head-fastest, in the
+    // planner's order, and the XCD that receives dispatch slot j gets units in
+    // runs of xcd_chunk: units that share K/V tiles (same head, neighbouring row
+    // tiles of one sequence) run on the same L2.  With Hk a multiple of 8 and
+    // runs of 1, every XCD serves whole K/V heads.
+    const unsigned wg = blockIdx.x;
+    const unsigned slot = wg >> 3, chunk = (unsigned)p.xcd_chunk;
+    const unsigned unit = ((slot / chunk) * 8u + (wg & 7u)) * chunk + slot % chunk;
+    const int hk = (int)(unit % (unsigned)p.Hk);
     const bool split = p.max_chunks > 1;
     const bool vec = p.vec != 0;
     const int D = p.D;
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
 
     // one workgroup per work item, in the planner's order (largest first);
     // workgroups past the end of the list exit
-    const int item_idx = blockIdx.x;
+    const int item_idx = (int)(unit / (unsigned)p.Hk);
     if (item_idx >= *p.item_count) return;
     Item it;
     {
@@ -605,44 +621,108 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             const unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
             const unsigned char* vbuf = kbuf + TILEB;
 
-            // ---- S^T = K Q^T for this wave's rows, one accumulator set per 32-key unit
+            // ---- S^T = K Q^T for this wave's rows, one accumulator set per 32-key unit.
+            // A lane's K operand rows: unit u adds 32 rows, which leaves the row
+            // swizzle (row mod 16) unchanged, so one base address per 16-key half
+            // serves every unit with a constant offset; k-step st is an XOR of the
+            // chunk position.  The fragments of k-step st+1 are read before the MFMAs
+            // of step st are issued, and two independent accumulator chains alternate
+            // (two 32-key units or the two 16-key halves, or even and odd k-steps when
+            // the tile has one 32x32 unit).
             constexpr int SPU = MR / 2;  // score values per lane per 32-key unit
             float sc[NU][SPU];
+            if constexpr (MR == 32) {
+                const int ln = opaque_lane();
+                const int kr = kappa32(ln & 31);
+                const int kbase = kr * ROWB + (((ln >> 5) ^ (kr & SWK)) << 4);
+                auto kread = [&](int u, int st) {
+                    return *reinterpret_cast<const u32x4*>(kbuf + (kbase ^ (st << 5)) + u * 32 * ROWB);
+                };
+                if constexpr (NU >= 2) {
+                    acc_t sacc[NU];
+                    u32x4 a[NU], nx[NU];
 #pragma unroll
-            for (int u = 0; u < NU; ++u) {
-                if constexpr (MR == 32) {
-                    // A row rho holds key u*32 + kappa(rho); kappa swaps bits 2 and 3.
-                    // Chunk st*2 + kgrp sits at position (st*2 + kgrp) ^ swz: the byte
-                    // offset is base ^ (st << 5) with base for st = 0.
-                    const int ln = opaque_lane();
-                    const int rl = ln & 31;
-                    const int kr = u * 32 + ((rl & ~12) | ((rl & 4) << 1) | ((rl & 8) >> 1));
-                    const int base = kr * ROWB + (((ln >> 5) ^ (kr & SWK)) << 4);
-                    acc_t s = {};
+                    for (int u = 0; u < NU; ++u) {
+                        sacc[u] = acc_t{};
+                        a[u] = kread(u, 0);
+                    }
 #pragma unroll
                     for (int st = 0; st < NKS; ++st) {
-                        const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + (base ^ (st << 5)));
-                        s = M::mma(a, qreg[st], s);
-                    }
+                        if (st + 1 < NKS) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) sc[u][v] = s[v];
-                } else {
-#pragma unroll
-                    for (int sb = 0; sb < 2; ++sb) {
-                        // chunk st*4 + kgrp at position (st*4 + kgrp) ^ swz = base ^ (st << 6)
-                        const int ln = opaque_lane();
-                        const int rl = ln & 15;
-                        const int kr = u * 32 + (rl >> 2) * 8 + sb * 4 + (rl & 3);
-                        const int base = kr * ROWB + (((ln >> 4) ^ (kr & SWK)) << 4);
-                        acc_t s = {};
-#pragma unroll
-                        for (int st = 0; st < NKS; ++st) {
-                            const u32x4 a = *reinterpret_cast<const u32x4*>(kbuf + (base ^ (st << 6)));
-                            s = M::mma(a, qreg[st], s);
+                            for (int u = 0; u < NU; ++u) nx[u] = kread(u, st + 1);
                         }
 #pragma unroll
-                        for (int v = 0; v < 4; ++v) sc[u][sb * 4 + v] = s[v];
+                        for (int u = 0; u < NU; ++u) sacc[u] = M::mma(a[u], qreg[st], sacc[u]);
+                        if (st + 1 < NKS) {
+#pragma unroll
+                            for (int u = 0; u < NU; ++u) a[u] = nx[u];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);  // keep the step order
                     }
+#pragma unroll
+                    for (int u = 0; u < NU; ++u)
+#pragma unroll
+                        for (int v = 0; v < 16; ++v) sc[u][v] = sacc[u][v];
+                } else {
+                    acc_t s0 = {}, s1 = {};
+                    u32x4 a0 = kread(0, 0), a1 = kread(0, 1);
+#pragma unroll
+                    for (int st = 0; st < NKS; st += 2) {
+                        u32x4 n0, n1;
+                        if (st + 2 < NKS) {
+                            n0 = kread(0, st + 2);
+                            n1 = kread(0, st + 3);
+                        }
+                        s0 = M::mma(a0, qreg[st], s0);
+                        s1 = M::mma(a1, qreg[st + 1], s1);
+                        if (st + 2 < NKS) {
+                            a0 = n0;
+                            a1 = n1;
+                        }
+                        __builtin_amdgcn_sched_barrier(0);  // keep the step order
+                    }
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) sc[0][v] = s0[v] + s1[v];
+                }
+            } else {
+                // chunk st*4 + kgrp at position (st*4 + kgrp) ^ swz = base ^ (st << 6);
+                // the two 16-key halves sb are the two chains
+                const int ln = opaque_lane();
+                const int rl = ln & 15;
+                int kbase[2];
+#pragma unroll
+                for (int sb = 0; sb < 2; ++sb) {
+                    const int kr = (rl >> 2) * 8 + sb * 4 + (rl & 3);
+                    kbase[sb] = kr * ROWB + (((ln >> 4) ^ (kr & SWK)) << 4);
+                }
+                auto kread = [&](int u, int sb, int st) {
+                    return *reinterpret_cast<const u32x4*>(kbuf + (kbase[sb] ^ (st << 6)) + u * 32 * ROWB);
+                };
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    acc_t sacc[2] = {acc_t{}, acc_t{}};
+                    u32x4 a[2], nx[2];
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb) a[sb] = kread(u, sb, 0);
+#pragma unroll
+                    for (int st = 0; st < NKS; ++st) {
+                        if (st + 1 < NKS) {
+#pragma unroll
+                            for (int sb = 0; sb < 2; ++sb) nx[sb] = kread(u, sb, st + 1);
+                        }
+#pragma unroll
+                        for (int sb = 0; sb < 2; ++sb) sacc[sb] = M::mma(a[sb], qreg[st], sacc[sb]);
+                        if (st + 1 < NKS) {
+#pragma unroll
+                            for (int sb = 0; sb < 2; ++sb) a[sb] = nx[sb];
+                        }
+                        __builtin_amdgcn_sched_barrier(0);  // keep the step order
+                    }
+#pragma unroll
+                    for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) sc[u][sb * 4 + v] = sacc[sb][v];
                 }
             }
 
@@ -710,13 +790,24 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             }
             l_run += rs;
 
-            // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  For d-block
-            // db the chunk index is db*(MR/8) + low bits, so the byte offset within
-            // the row is base ^ (db * MR * 2) with base computed for db = 0.
+            // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  Per tile, the
+            // lane's two read addresses (rows r0, r0 + 4) are built for the first 16
+            // keys and each XOR pattern of the swizzled chunk bits; other 16-key
+            // groups add whole rows (the swizzle depends on the row mod 8 only) and
+            // d-blocks past the swizzled bits add a whole chunk group, both constants.
             {
                 const int ln = opaque_lane();
-                const int g16 = ln >> 4;
-                const int a16 = ln & 15;
+                const int g16 = ln >> 4, a16 = ln & 15;
+                const int r0 = (MR == 32) ? (g16 >> 1) * 8 + (a16 >> 2) : g16 * 8 + (a16 >> 2);
+                const int c0 = (MR == 32) ? (g16 & 1) * 2 + ((a16 >> 1) & 1) : (a16 >> 1) & 1;
+                int vx[NPAT][2];
+#pragma unroll
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    const int rr = r0 + 4 * h2;
+                    const int bx = rr * ROWB + ((c0 ^ ((2 * rr) & SWV)) << 4) + (a16 & 1) * 8;
+#pragma unroll
+                    for (int pat = 0; pat < NPAT; ++pat) vx[pat][h2] = bx ^ ((pat * CPD) << 4);
+                }
 #pragma unroll
                 for (int u = 0; u < NU; ++u) {
                     if constexpr (MR == 32) {
@@ -724,30 +815,22 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                         for (int ts = 0; ts < 2; ++ts) {
                             const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
                                                   pk[u][ts * 4 + 3]};
-                            const int r0 = u * 32 + ts * 16 + (g16 >> 1) * 8 + (a16 >> 2);
-                            const int r1 = r0 + 4;
-                            const int c0 = (g16 & 1) * 2 + ((a16 >> 1) & 1);
-                            const int b0 = r0 * ROWB + ((c0 ^ ((2 * r0) & SWV)) << 4) + (a16 & 1) * 8;
-                            const int b1 = r1 * ROWB + ((c0 ^ ((2 * r1) & SWV)) << 4) + (a16 & 1) * 8;
 #pragma unroll
                             for (int db = 0; db < NDB; ++db) {
-                                const u32x2 lo2 = lds_read_tr16(vbuf + (b0 ^ (db << 6)));
-                                const u32x2 hi2 = lds_read_tr16(vbuf + (b1 ^ (db << 6)));
+                                const int off = (u * 32 + ts * 16) * ROWB + (db / NPAT) * (NPAT * CPD * 16);
+                                const u32x2 lo2 = lds_read_tr16(vbuf + vx[db % NPAT][0] + off);
+                                const u32x2 hi2 = lds_read_tr16(vbuf + vx[db % NPAT][1] + off);
                                 const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
                                 o[db] = M::mma(a, b, o[db]);
                             }
                         }
                     } else {
                         const u32x4 b = u32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
-                        const int r0 = u * 32 + g16 * 8 + (a16 >> 2);
-                        const int r1 = r0 + 4;
-                        const int c0 = (a16 >> 1) & 1;
-                        const int b0 = r0 * ROWB + ((c0 ^ ((2 * r0) & SWV)) << 4) + (a16 & 1) * 8;
-                        const int b1 = r1 * ROWB + ((c0 ^ ((2 * r1) & SWV)) << 4) + (a16 & 1) * 8;
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
-                            const u32x2 lo2 = lds_read_tr16(vbuf + (b0 ^ (db << 5)));
-                            const u32x2 hi2 = lds_read_tr16(vbuf + (b1 ^ (db << 5)));
+                            const int off = u * 32 * ROWB + (db / NPAT) * (NPAT * CPD * 16);
+                            const u32x2 lo2 = lds_read_tr16(vbuf + vx[db % NPAT][0] + off);
+                            const u32x2 hi2 = lds_read_tr16(vbuf + vx[db % NPAT][1] + off);
                             const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
                             o[db] = M::mma(a, b, o[db]);
                         }
@@ -853,7 +936,10 @@ hipError_t g_last = hipSuccess;
 
 template <int DP, int MR, int WR, int BN, int NS>
 hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
-    dim3 grid((unsigned)plan.items_bound, (unsigned)p.Hk);
+    // one workgroup per (item, K/V head) unit, padded to whole runs on all 8 XCDs
+    const int64_t units = plan.items_bound * (int64_t)p.Hk;
+    const int64_t run = 8 * (int64_t)p.xcd_chunk;
+    dim3 grid((unsigned)((units + run - 1) / run * run));
     hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
     return hipGetLastError();
 }
@@ -948,6 +1034,10 @@ int make_plan(const Shapes& s, Plan* plan) {
     const int64_t tiles = (s.total_q * G + P.rows - 1) / P.rows + s.batch;
     const int64_t items = tiles * P.max_chunks;
     if (items >= INT32_MAX / 2 || s.Hk > 65535) return FA_ERR_ARGUMENT;
+    // runs of units per XCD: whole heads when Hk is a multiple of 8, else runs of
+    // 8 units (neighbouring items of one head for Hk = 1)
+    P.xcd_chunk = (s.Hk % 8 == 0) ? 1 : 8;
+    if ((items * s.Hk + 64) * 8 >= (int64_t)UINT32_MAX / 2) return FA_ERR_ARGUMENT;
     P.items_bound = items;
     // workspace: [split partials o][split partials lse][items][count][seq offsets]
     size_t off = 0;
@@ -974,6 +1064,7 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     FwdParams p = p_in;
     p.rows = plan.rows;
     p.items_bound = (int32_t)plan.items_bound;
+    p.xcd_chunk = plan.xcd_chunk;
     hipError_t e = hipSuccess;
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
     e = hipGetLastError();

@@ -33,6 +33,7 @@ struct FwdParams {
     int32_t max_chunks;
     int32_t rows;           // rows per work item (MFMA rows per wave * waves)
     int32_t items_bound;    // upper bound of the number of work items per K/V head
+    int32_t xcd_chunk;      // work units per run on one XCD (grid remap)
     int4* items;            // work list: per item {b, rt, c | nc<<16, 0}, {q0, Lq, k0, Lk}
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
@@ -64,6 +65,7 @@ struct Plan {
     int chunk;      // keys per split
     int max_chunks; // upper bound of splits per sequence
     int64_t items_bound;  // upper bound of work items per K/V head
+    int xcd_chunk;        // work units per run on one XCD
     size_t off_items, off_count, off_seq, off_tok;  // workspace layout (bytes)
     size_t ws_bytes;
 };
