@@ -39,12 +39,15 @@ def _load():
         if not os.path.exists(_LIB):
             build()
         lib = ctypes.CDLL(_LIB)
-        f = lib.fa_oracle_attention
+        f = lib.fa_oracle_attention_t
         P = ctypes.c_void_p
         f.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int,
-                      ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int]
+                      ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int]
         f.restype = ctypes.c_int
+        w = lib.fa_oracle_widen
+        w.argtypes = [P, ctypes.c_int64, ctypes.c_int, P]
+        w.restype = None
         g = lib.fa_oracle_kv_append
         g.argtypes = [P, P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P,
                       ctypes.c_int, ctypes.c_int, ctypes.c_int64, P, P]
@@ -53,12 +56,26 @@ def _load():
     return _lib
 
 
-def _bits(t) -> np.ndarray:
-    """bf16 tensor / uint16 array -> contiguous uint16 numpy array of its bits."""
+DTYPES = {"bf16": 0, "f16": 1}
+
+
+def _dtype_of(t) -> str:
+    """'bf16' or 'f16' for a torch tensor; uint16 bit arrays are taken as bf16."""
     try:
         import torch
         if isinstance(t, torch.Tensor):
-            assert t.dtype == torch.bfloat16, t.dtype
+            return {torch.bfloat16: "bf16", torch.float16: "f16"}[t.dtype]
+    except ImportError:  # pragma: no cover
+        pass
+    return "bf16"
+
+
+def _bits(t) -> np.ndarray:
+    """bf16 / fp16 tensor or uint16 array -> contiguous uint16 numpy array of its bits."""
+    try:
+        import torch
+        if isinstance(t, torch.Tensor):
+            assert t.dtype in (torch.bfloat16, torch.float16), t.dtype
             return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
     except ImportError:  # pragma: no cover
         pass
@@ -78,7 +95,7 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None, page_block_
               softmax_scale: float = 1.0, window_left: int = -1, window_right: int = -1,
               token_sel: Optional[np.ndarray] = None, nthreads: Optional[int] = None
               ) -> Tuple[np.ndarray, np.ndarray]:
-    """fp64 attention over host bf16 inputs.
+    """fp64 attention over host bf16 or fp16 inputs (q, k, v of one element type).
 
     q: (total_q, H, D); k, v: (total_k, Hk, D) or, with ``block_table``,
     (num_blocks, page_block_size, Hk, D).  Returns ``out`` (total_q, H, D) float64
@@ -108,15 +125,25 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None, page_block_
     if token_sel is not None:
         sel = np.ascontiguousarray(token_sel, dtype=np.uint8)
         assert sel.shape == (total_q,)
-    rc = lib.fa_oracle_attention(qb.ctypes.data, total_q, H, D, kb.ctypes.data, vb.ctypes.data,
-                                 kv_rows, page, Hk, cu_q.ctypes.data, cu_k.ctypes.data, batch,
-                                 bt_ptr, width, float(softmax_scale), int(window_left),
-                                 int(window_right), None if sel is None else sel.ctypes.data,
-                                 out.ctypes.data, lse.ctypes.data,
-                                 int(nthreads or default_threads()))
+    dt = _dtype_of(q)
+    assert _dtype_of(k) == dt and _dtype_of(v) == dt, "q, k and v must share one element type"
+    rc = lib.fa_oracle_attention_t(qb.ctypes.data, total_q, H, D, kb.ctypes.data, vb.ctypes.data,
+                                   kv_rows, page, Hk, cu_q.ctypes.data, cu_k.ctypes.data, batch,
+                                   bt_ptr, width, float(softmax_scale), int(window_left),
+                                   int(window_right), None if sel is None else sel.ctypes.data,
+                                   out.ctypes.data, lse.ctypes.data,
+                                   int(nthreads or default_threads()), DTYPES[dt])
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return out, lse
+
+
+def widen(bits, dtype: str) -> np.ndarray:
+    """The oracle's exact widening of 16-bit values ('bf16' or 'f16') to float64."""
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(a.shape, dtype=np.float64)
+    _load().fa_oracle_widen(a.ctypes.data, a.size, DTYPES[dtype], out.ctypes.data)
+    return out
 
 
 def attention_workload(wl, token_sel=None, nthreads=None):

@@ -35,7 +35,9 @@
  * diagonal, with causal = (window_left < 0, window_right = 0), and GQA heads
  * grouped contiguously.
  *
- * Numerics: inputs are bf16 widened exactly to double; every sum is a plain
+ * Numerics: inputs are bf16 or IEEE binary16 (fp16) widened exactly to double
+ * (the element type the candle wrapper is generic over: page "flash-attn-varlen
+ * paged expects k/v tensors of rank 4", section Source); every sum is a plain
  * left-to-right double sum; the softmax is the two-pass stable form (max, then
  * exp and sum).  Work items (sequence, head) are spread over POSIX threads.
  */
@@ -52,8 +54,27 @@ static double bf16_to_double(uint16_t h) {
     return (double)f;
 }
 
+/* IEEE 754 binary16: sign, 5-bit exponent (bias 15), 10-bit fraction. */
+static double f16_to_double(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 31, m = h & 1023;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24); /* subnormal: m * 2^-14 / 1024 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* Test hook: widen n 16-bit values (dtype 0 = bf16, 1 = fp16) to double. */
+void fa_oracle_widen(const uint16_t *in, int64_t n, int dtype, double *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = dtype ? f16_to_double(in[i]) : bf16_to_double(in[i]);
+}
+
 typedef struct {
     const uint16_t *q, *k, *v;
+    int f16;               /* element type: 0 = bf16, 1 = fp16 */
     int64_t total_q;
     int num_heads, num_heads_k, head_dim;
     int64_t kv_rows;       /* total_k (non-paged) or num_blocks (paged) */
@@ -119,7 +140,10 @@ static void run_item(job_t *J, int b, int h, double *s, int64_t *koff) {
             if (!key_visible(J, i, j, Lq, Lk)) continue;
             const uint16_t *krow = J->k + koff[j];
             double dot = 0.0;
-            for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
+            if (J->f16)
+                for (int d = 0; d < D; ++d) dot += f16_to_double(qrow[d]) * f16_to_double(krow[d]);
+            else
+                for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
             s[j] = J->scale * dot;
             if (s[j] > m) m = s[j];
             ++n_visible;
@@ -135,7 +159,10 @@ static void run_item(job_t *J, int b, int h, double *s, int64_t *koff) {
             double p = exp(s[j] - m);
             l += p;
             const uint16_t *vrow = J->v + koff[j];
-            for (int d = 0; d < D; ++d) orow[d] += p * bf16_to_double(vrow[d]);
+            if (J->f16)
+                for (int d = 0; d < D; ++d) orow[d] += p * f16_to_double(vrow[d]);
+            else
+                for (int d = 0; d < D; ++d) orow[d] += p * bf16_to_double(vrow[d]);
         }
         for (int d = 0; d < D; ++d) orow[d] /= l;
         J->lse[(int64_t)h * J->total_q + t] = m + log(l);
@@ -165,7 +192,7 @@ static void *worker(void *arg) {
 
 /*
  * All arrays are host memory, contiguous, row-major:
- *   q    [total_q][num_heads][head_dim]           bf16 bits
+ *   q    [total_q][num_heads][head_dim]           bf16 (dtype 0) or fp16 (dtype 1) bits
  *   k, v [kv_rows][num_heads_k][head_dim]          (page == 0)
  *        [kv_rows][page][num_heads_k][head_dim]    (page  > 0, kv_rows = num_blocks)
  *   cu_q, cu_k [batch+1]  int32 cumulative lengths
@@ -175,12 +202,12 @@ static void *worker(void *arg) {
  * Returns 0, or -1 for bad arguments, -2 for a block id / row outside the pool,
  * -3 when memory runs out.
  */
-int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int head_dim,
-                        const uint16_t *k, const uint16_t *v, int64_t kv_rows, int page,
-                        int num_heads_k, const int32_t *cu_q, const int32_t *cu_k, int batch,
-                        const int32_t *block_table, int bt_width, double scale,
-                        int window_left, int window_right, const uint8_t *token_sel,
-                        double *out, double *lse, int nthreads) {
+int fa_oracle_attention_t(const uint16_t *q, int64_t total_q, int num_heads, int head_dim,
+                          const uint16_t *k, const uint16_t *v, int64_t kv_rows, int page,
+                          int num_heads_k, const int32_t *cu_q, const int32_t *cu_k, int batch,
+                          const int32_t *block_table, int bt_width, double scale,
+                          int window_left, int window_right, const uint8_t *token_sel,
+                          double *out, double *lse, int nthreads, int dtype) {
     if (num_heads <= 0 || num_heads_k <= 0 || head_dim <= 0 || batch < 0) return -1;
     if (num_heads % num_heads_k != 0) return -1;
     if (page < 0 || (page > 0 && !block_table)) return -1;
@@ -189,7 +216,8 @@ int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int h
         if (cu_q[b + 1] < cu_q[b] || cu_k[b + 1] < cu_k[b]) return -1;
     job_t J;
     memset(&J, 0, sizeof J);
-    J.q = q; J.k = k; J.v = v; J.total_q = total_q;
+    if (dtype != 0 && dtype != 1) return -1;
+    J.q = q; J.k = k; J.v = v; J.total_q = total_q; J.f16 = dtype;
     J.num_heads = num_heads; J.num_heads_k = num_heads_k; J.head_dim = head_dim;
     J.kv_rows = kv_rows; J.page = page; J.cu_q = cu_q; J.cu_k = cu_k; J.batch = batch;
     J.block_table = block_table; J.bt_width = bt_width; J.scale = scale;
@@ -206,6 +234,18 @@ int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int h
     if (J.error == 1) return -2;
     if (J.error == 2) return -3;
     return 0;
+}
+
+/* bf16 entry (dtype 0). */
+int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int head_dim,
+                        const uint16_t *k, const uint16_t *v, int64_t kv_rows, int page,
+                        int num_heads_k, const int32_t *cu_q, const int32_t *cu_k, int batch,
+                        const int32_t *block_table, int bt_width, double scale,
+                        int window_left, int window_right, const uint8_t *token_sel,
+                        double *out, double *lse, int nthreads) {
+    return fa_oracle_attention_t(q, total_q, num_heads, head_dim, k, v, kv_rows, page, num_heads_k, cu_q,
+                                 cu_k, batch, block_table, bt_width, scale, window_left, window_right,
+                                 token_sel, out, lse, nthreads, 0);
 }
 
 /*

@@ -50,11 +50,15 @@ def _threads() -> int:
     return max(1, min(16, n))
 
 
-def normal_bf16(rng: np.random.Generator, shape: Sequence[int]) -> torch.Tensor:
-    """N(0,1) float32 draws rounded to bf16, shape ``shape`` (CPU tensor)."""
+TORCH_DTYPES = {"bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def normal_bf16(rng: np.random.Generator, shape: Sequence[int], dtype: str = "bf16") -> torch.Tensor:
+    """N(0,1) float32 draws rounded (nearest even) to bf16, or to fp16 with
+    ``dtype="f16"``, shape ``shape`` (CPU tensor).  The draws do not depend on dtype."""
     shape = tuple(int(s) for s in shape)
     n = int(np.prod(shape)) if shape else 1
-    out = torch.empty(n, dtype=torch.bfloat16)
+    out = torch.empty(n, dtype=TORCH_DTYPES[dtype])
     if n <= _CHUNK:
         if n:
             out.copy_(torch.from_numpy(rng.standard_normal(n, dtype=np.float32)))
@@ -216,7 +220,7 @@ def make_custom(lens_q: Sequence[int], lens_k: Sequence[int], num_heads: int, nu
                 head_dim: int, *, seed: int = 0, page: int = 0, width: int = 0,
                 window_left: int = -1, window_right: int = 0, scale: Optional[float] = None,
                 spare: float = 0.1, poison: bool = False, rng: Optional[np.random.Generator] = None,
-                name: str = "custom") -> Workload:
+                name: str = "custom", dtype: str = "bf16") -> Workload:
     """Build a workload from explicit lengths.
 
     ``page > 0`` makes a paged pool of ``ceil((1+spare) * sum(ceil(Lk/page)))``
@@ -250,9 +254,9 @@ def make_custom(lens_q: Sequence[int], lens_k: Sequence[int], num_heads: int, nu
             bt[b, :np_] = perm[pos:pos + np_]
             pos += np_
         block_table = bt
-        q = normal_bf16(rng, (total_q, num_heads, head_dim))
-        k = normal_bf16(rng, (num_blocks, page, num_heads_k, head_dim))
-        v = normal_bf16(rng, (num_blocks, page, num_heads_k, head_dim))
+        q = normal_bf16(rng, (total_q, num_heads, head_dim), dtype)
+        k = normal_bf16(rng, (num_blocks, page, num_heads_k, head_dim), dtype)
+        v = normal_bf16(rng, (num_blocks, page, num_heads_k, head_dim), dtype)
         if poison:
             used = np.zeros((num_blocks, page), dtype=bool)
             for b in range(batch):
@@ -262,9 +266,9 @@ def make_custom(lens_q: Sequence[int], lens_k: Sequence[int], num_heads: int, nu
             k[mask] = float("nan")
             v[mask] = float("nan")
     else:
-        q = normal_bf16(rng, (total_q, num_heads, head_dim))
-        k = normal_bf16(rng, (total_k, num_heads_k, head_dim))
-        v = normal_bf16(rng, (total_k, num_heads_k, head_dim))
+        q = normal_bf16(rng, (total_q, num_heads, head_dim), dtype)
+        k = normal_bf16(rng, (total_k, num_heads_k, head_dim), dtype)
+        v = normal_bf16(rng, (total_k, num_heads_k, head_dim), dtype)
     return Workload(name=name, seed=seed, q=q, k=k, v=v, cu_seqlens_q=_cu(lens_q),
                     cu_seqlens_k=_cu(lens_k), block_table=block_table, page_block_size=page,
                     softmax_scale=_f32(scale), window_left=int(window_left),
@@ -285,19 +289,19 @@ def make_append(lens_new: Sequence[int], lens_k: Sequence[int], num_heads_k: int
 
 
 def make_padded(B: int, Sq: int, Sk: int, num_heads: int, num_heads_k: int, head_dim: int, *,
-                seed: int = 0, layout: str = "bshd"):
+                seed: int = 0, layout: str = "bshd", dtype: str = "bf16"):
     """Padded inputs q (B, Sq, H, D), k/v (B, Sk, Hk, D) bf16, drawn q, k, v in that
     order.  ``layout="bhsd"`` draws them head-major, (B, H, S, D) contiguous, and
     returns (B, S, H, D) views of those (strided, not mergeable into tokens)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     if layout == "bhsd":
-        q = normal_bf16(rng, (B, num_heads, Sq, head_dim)).transpose(1, 2)
-        k = normal_bf16(rng, (B, num_heads_k, Sk, head_dim)).transpose(1, 2)
-        v = normal_bf16(rng, (B, num_heads_k, Sk, head_dim)).transpose(1, 2)
+        q = normal_bf16(rng, (B, num_heads, Sq, head_dim), dtype).transpose(1, 2)
+        k = normal_bf16(rng, (B, num_heads_k, Sk, head_dim), dtype).transpose(1, 2)
+        v = normal_bf16(rng, (B, num_heads_k, Sk, head_dim), dtype).transpose(1, 2)
     else:
-        q = normal_bf16(rng, (B, Sq, num_heads, head_dim))
-        k = normal_bf16(rng, (B, Sk, num_heads_k, head_dim))
-        v = normal_bf16(rng, (B, Sk, num_heads_k, head_dim))
+        q = normal_bf16(rng, (B, Sq, num_heads, head_dim), dtype)
+        k = normal_bf16(rng, (B, Sk, num_heads_k, head_dim), dtype)
+        v = normal_bf16(rng, (B, Sk, num_heads_k, head_dim), dtype)
     return q, k, v
 
 
@@ -330,7 +334,7 @@ def append_config(name: str, seed: Optional[int] = None) -> Workload:
     return wl
 
 
-def make_config(name: str, seed: Optional[int] = None, *, poison: bool = False) -> Workload:
+def make_config(name: str, seed: Optional[int] = None, *, poison: bool = False, dtype: str = "bf16") -> Workload:
     """The named workload (``c1`` ... ``c5b``) for ``seed`` (default: its timing seed)."""
     cfg = CONFIGS[name]
     if seed is None:
@@ -340,6 +344,6 @@ def make_config(name: str, seed: Optional[int] = None, *, poison: bool = False) 
     wl = make_custom(lens_q, lens_k, cfg["num_heads"], cfg["num_heads_k"], cfg["head_dim"],
                      seed=seed, page=cfg["page"], width=cfg["width"],
                      window_left=cfg["window_left"], window_right=cfg["window_right"],
-                     scale=cfg["scale"], poison=poison, rng=rng, name=name)
+                     scale=cfg["scale"], poison=poison, rng=rng, name=name, dtype=dtype)
     wl.extra["desc"] = cfg["desc"]
     return wl
