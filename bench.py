@@ -285,7 +285,7 @@ def cpu_append_baseline(wl, k_new, v_new, work):
 def bench_append(args, fa, W, hip, dev, stream):
     import torch
     print("bench: generating %s (append)" % args.workload, file=sys.stderr, flush=True)
-    wl = W.append_config(args.workload, args.seed)
+    wl = W.append_config(args.workload, args.seed, dtype=args.dtype)
     work = append_work(wl)
     # new rows: the pool rows of each sequence's last Lq keys (what a decode or
     # chunked-prefill step appends); rotated copies keep them out of the MALL
@@ -367,8 +367,8 @@ def bench_append(args, fa, W, hip, dev, stream):
         "value": round(work["total_bytes"] / (ms_per_step * 1e-3) / 1e9, 3),
         "unit": "GB/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, seed %d)" % wl.seed,
+        "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,1) %s, seed %d)" % (args.dtype, wl.seed),
         "config": {
             "workload": "append into %s: %s" % (args.workload, wl.extra.get("desc", "")),
             "batch": wl.batch, "total_new": work["total_new"], "num_heads_k": Hk, "head_dim": D,
@@ -396,7 +396,7 @@ def bench_padded(args, fa, W, hip, dev, stream):
     B, Sq, Sk, H, Hk, D = (cfg[x] for x in ("B", "Sq", "Sk", "num_heads", "num_heads_k", "head_dim"))
     seed = cfg["seed"] if args.seed is None else args.seed
     print("bench: generating %s (padded)" % args.workload, file=sys.stderr, flush=True)
-    q, k, v = W.make_padded(B, Sq, Sk, H, Hk, D, seed=seed)
+    q, k, v = W.make_padded(B, Sq, Sk, H, Hk, D, seed=seed, dtype=args.dtype)
     scale = float(np.float32(1.0 / math.sqrt(D)))
     # the equivalent varlen description (uniform offsets) gives the algorithmic work
     # and feeds the oracle's CPU leg
@@ -474,7 +474,8 @@ def bench_padded(args, fa, W, hip, dev, stream):
         "metric": "padded (batch-major) attention: prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)",
         "value": round(value, 3), "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic (seeded N(0,1) bf16, seed %d)" % seed,
+        "vs_baseline": None, "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,1) %s, seed %d)" % (args.dtype, seed),
         "config": {"workload": "%s: %s" % (args.workload, cfg["desc"]), "batch": B, "seqlen_q": Sq,
                    "seqlen_k": Sk, "num_heads": H, "num_heads_k": Hk, "head_dim": D,
                    "window_left": cfg["window_left"], "window_right": cfg["window_right"],
@@ -500,6 +501,8 @@ def main(argv=None):
     ap.add_argument("--workload", default=None,
                     help="c1..c5b (forward, append; default c2) or p2/p4 (padded; default p4)")
     ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
+                    help="element type of q/k/v/out (and the append's rows and pools)")
     ap.add_argument("--op", default="fwd", choices=["fwd", "append", "padded"],
                     help="fwd: the attention forward (default); append: the paged K/V append; "
                          "padded: the batch-major entry")
@@ -552,7 +555,7 @@ def main(argv=None):
     if args.op == "padded":
         return bench_padded(args, fa, W, hip, dev, stream)
     print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
-    wl = W.make_config(args.workload, args.seed)
+    wl = W.make_config(args.workload, args.seed, dtype=args.dtype)
     work = work_of(wl)
     decode = args.workload in DECODE
 
@@ -661,8 +664,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded N(0,1) bf16, seed %d)" % wl.seed,
+        "dtype": args.dtype,
+        "data": "synthetic (seeded N(0,1) %s, seed %d)" % (args.dtype, wl.seed),
         "config": {
             "workload": "%s: %s" % (args.workload, wl.extra.get("desc", "")),
             "batch": wl.batch, "total_q": int(wl.lens_q.sum()), "total_k": int(wl.lens_k.sum()),

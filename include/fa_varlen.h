@@ -49,8 +49,11 @@
 extern "C" {
 #endif
 
-/* element types */
-enum fa_dtype { FA_DTYPE_BF16 = 1, FA_DTYPE_I32 = 2 };
+/* element types: q/k/v/out (and the append's rows and pools) are all bf16 or
+ * all IEEE binary16 (fp16) -- the candle wrapper is generic over the element
+ * type (page "flash-attn-varlen paged expects k/v tensors of rank 4", Source);
+ * block tables are int32 */
+enum fa_dtype { FA_DTYPE_BF16 = 1, FA_DTYPE_I32 = 2, FA_DTYPE_F16 = 3 };
 
 /* status codes */
 enum fa_status {
@@ -60,7 +63,7 @@ enum fa_status {
     FA_ERR_SHAPE = 3,        /* shapes disagree */
     FA_ERR_PAGE_SIZE = 4,    /* page_block_size missing, mismatched or not a multiple of 32 */
     FA_ERR_HEAD_DIM = 5,     /* head_dim > 512 or < 1 */
-    FA_ERR_DTYPE = 6,        /* not bf16 (tensors) / int32 (block_table) */
+    FA_ERR_DTYPE = 6,        /* tensors not all bf16 or all fp16 / block_table not int32 */
     FA_ERR_ARGUMENT = 7,     /* null pointer, negative batch, heads not divisible, size limits */
     FA_ERR_WORKSPACE = 8,    /* workspace missing or smaller than fa_varlen_workspace_bytes() */
     FA_ERR_DEVICE = 9,       /* a pointer is not device memory */
@@ -84,10 +87,10 @@ typedef struct fa_tensor {
  * fa_varlen_check -- the shape/stride/dtype contract alone.  Pure host code:
  * no pointer is dereferenced and no HIP call is made, so it runs without a GPU.
  *
- *   q            (total_q, num_heads, head_dim) bf16, last dim contiguous
+ *   q            (total_q, num_heads, head_dim) bf16 or fp16, last dim contiguous
  *   k, v         paged: (num_blocks, page_block_size, num_heads_k, head_dim)
- *                non-paged: (total_k, num_heads_k, head_dim); bf16, last dim contiguous
- *   out          same shape as q, bf16, last dim contiguous (may be NULL here)
+ *                non-paged: (total_k, num_heads_k, head_dim); same dtype as q, last dim contiguous
+ *   out          same shape and dtype as q, last dim contiguous (may be NULL here)
  *   batch        number of sequences (>= 0)
  *   block_table  NULL = non-paged; else int32 (batch, max_blocks_per_seq), last dim contiguous
  *   page_block_size  0 = not given; must equal k.shape[1] and be a multiple of 32 when paged;
@@ -147,9 +150,10 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
  * computes exactly what fa_varlen_fwd computes with cu_seqlens_q = b * Sq and
  * cu_seqlens_k = b * Sk (no cu arrays are needed).
  *
- *   q, out   (B, Sq, H, D) bf16, last dim contiguous, any other strides
- *            (for instance a (B, H, S, D) tensor viewed as (B, S, H, D)).
- *   k, v     (B, Sk, Hk, D) bf16, last dim contiguous, same shape; H % Hk == 0;
+ *   q, out   (B, Sq, H, D) bf16 or fp16 (one dtype for q, k, v and out), last
+ *            dim contiguous, any other strides (for instance a (B, H, S, D)
+ *            tensor viewed as (B, S, H, D)).
+ *   k, v     (B, Sk, Hk, D), last dim contiguous, same shape; H % Hk == 0;
  *            1 <= D <= 512; B*Sq*H and B*Sk below 2^31.
  *   softmax_scale, window_left, window_right  as for fa_varlen_fwd (query row i
  *            sits at key position i + Sk - Sq).
@@ -182,7 +186,7 @@ int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t b
  * tensors of rank 4" and "page_block_size ... does not match k shape", What it
  * means: logical key n of sequence b is block block_table[b][n / P], slot n % P).
  *
- *   k_new, v_new   (total_new, num_heads_k, head_dim) bf16, last dim contiguous,
+ *   k_new, v_new   (total_new, num_heads_k, head_dim) bf16 or fp16, last dim contiguous,
  *                  same shape; read only.
  *   cu_seqlens_new device int32 [batch+1], cumulative new-token counts from 0:
  *                  sequence b owns rows [cu_new[b], cu_new[b+1]) of k_new/v_new.
@@ -191,7 +195,7 @@ int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t b
  *                  are each sequence's last keys: new token j of sequence b goes to
  *                  logical position Lk_b - Lnew_b + j.
  *   block_table    int32 (batch, max_blocks), last dim contiguous.
- *   k_cache, v_cache  (num_blocks, page_block_size, num_heads_k, head_dim) bf16,
+ *   k_cache, v_cache  (num_blocks, page_block_size, num_heads_k, head_dim), dtype of k_new,
  *                  last dim contiguous, same shape; written in place.
  *   page_block_size  must equal k_cache.shape[1] and be a multiple of 32; the
  *                  head size is at most 512 (the paged forward's rules and texts).

@@ -339,3 +339,20 @@ def test_padded_workspace_and_empty_call(lib):
     # no batch or no query: nothing is launched, no pointer is inspected
     assert fa.fa_padded_fwd(desc([0, 5, 4, 64]), desc([0, 9, 2, 64]), desc([0, 9, 2, 64]),
                             desc([0, 5, 4, 64]), 0.1, -1, 0, 0, 0, 0, 0) == 0
+
+
+def test_f16_accepted_and_dtypes_must_match(lib):
+    from varlen_flash_attention_fa_amd import FA_DTYPE_F16
+    code = {v: k for k, v in fa.STATUS.items()}
+    q, k = desc([86, 4, 64], dtype=FA_DTYPE_F16), desc([86, 2, 64], dtype=FA_DTYPE_F16)
+    assert check(q, k, k, out=desc([86, 4, 64], dtype=FA_DTYPE_F16))[0] == 0
+    # mixed element types are rejected: q/k/v, and out
+    assert check(q, K3, K3)[0] == code["FA_ERR_DTYPE"]
+    assert check(q, k, K3)[0] == code["FA_ERR_DTYPE"]
+    assert check(q, k, k, out=desc([86, 4, 64]))[0] == code["FA_ERR_DTYPE"]
+    kn, kc = desc([6, 2, 64], dtype=FA_DTYPE_F16), desc([10, 32, 2, 64], dtype=FA_DTYPE_F16)
+    assert acheck(kn=kn, vn=kn, kc=kc, vc=kc)[0] == 0
+    assert acheck(kn=kn, vn=kn)[0] == code["FA_ERR_DTYPE"]
+    qp, kp = desc([2, 5, 4, 64], dtype=FA_DTYPE_F16), desc([2, 9, 2, 64], dtype=FA_DTYPE_F16)
+    assert pcheck(q=qp, k=kp, v=kp)[0] == 0
+    assert pcheck(q=qp)[0] == code["FA_ERR_DTYPE"]

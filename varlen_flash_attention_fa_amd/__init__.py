@@ -23,7 +23,7 @@ __all__ = [
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
     "fa_varlen_set_kernel_events", "fa_kv_append_check", "fa_kv_append", "kv_append",
     "fa_padded_check", "fa_padded_workspace_bytes", "fa_padded_fwd", "padded_fwd",
-    "FA_DTYPE_BF16", "FA_DTYPE_I32", "STATUS",
+    "FA_DTYPE_BF16", "FA_DTYPE_I32", "FA_DTYPE_F16", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +31,7 @@ _LIB_PATH = os.path.join(_HERE, "libfa_varlen.so")
 
 FA_DTYPE_BF16 = 1
 FA_DTYPE_I32 = 2
+FA_DTYPE_F16 = 3
 STATUS = {0: "FA_OK", 1: "FA_ERR_RANK", 2: "FA_ERR_CONTIGUOUS", 3: "FA_ERR_SHAPE",
           4: "FA_ERR_PAGE_SIZE", 5: "FA_ERR_HEAD_DIM", 6: "FA_ERR_DTYPE", 7: "FA_ERR_ARGUMENT",
           8: "FA_ERR_WORKSPACE", 9: "FA_ERR_DEVICE", 10: "FA_ERR_HIP"}
@@ -117,7 +118,7 @@ def desc(shape: Sequence[int], stride: Optional[Sequence[int]] = None, dtype: in
 
 def _tdesc(t) -> FaTensor:
     import torch
-    dt = {torch.bfloat16: FA_DTYPE_BF16, torch.int32: FA_DTYPE_I32}.get(t.dtype, 0)
+    dt = {torch.bfloat16: FA_DTYPE_BF16, torch.int32: FA_DTYPE_I32, torch.float16: FA_DTYPE_F16}.get(t.dtype, 0)
     return desc(list(t.shape), list(t.stride()), dt, t.data_ptr())
 
 
@@ -265,7 +266,7 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,
                out=None, workspace=None, stream=None):
     """Varlen flash-attention forward on device tensors.
 
-    q (total_q, H, D) bf16; k/v (total_k, Hk, D) or paged (num_blocks, P, Hk, D)
+    q (total_q, H, D) bf16 or fp16; k/v (total_k, Hk, D) or paged (num_blocks, P, Hk, D), q's dtype,
     with ``block_table`` (batch, max_blocks) int32; cu_seqlens_* int32 (batch+1,).
     Returns ``out`` (same shape as q), plus ``lse`` (H, total_q) fp32 if
     ``return_lse``.  Allocates out / lse / workspace with torch when not given and

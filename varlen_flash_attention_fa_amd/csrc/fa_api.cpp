@@ -24,6 +24,8 @@
 
 namespace {
 
+bool is_elem16(int32_t dt) { return dt == FA_DTYPE_BF16 || dt == FA_DTYPE_F16; }
+
 thread_local std::string g_err;
 thread_local void* g_ev_start = nullptr;
 thread_local void* g_ev_stop = nullptr;
@@ -61,8 +63,8 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
     for (const fa_tensor* t : {q, k, v})
         if (t->rank < 0 || t->rank > 4)
             return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
-    if (q->dtype != FA_DTYPE_BF16 || k->dtype != FA_DTYPE_BF16 || v->dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_DTYPE, "flash-attn-varlen takes bf16 q/k/v (dtype codes q: %d, k: %d, v: %d)",
+    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(FA_ERR_DTYPE, "flash-attn-varlen takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
                     (int)q->dtype, (int)k->dtype, (int)v->dtype);
 
     const bool paged = bt != nullptr;
@@ -131,8 +133,9 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
                 return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(t, false).c_str(),
                             dims(t, true).c_str());
     if (out) {
-        if (out->dtype != FA_DTYPE_BF16)
-            return fail(FA_ERR_DTYPE, "out must be bf16 (dtype code %d)", (int)out->dtype);
+        if (out->dtype != q->dtype)
+            return fail(FA_ERR_DTYPE, "out must have the dtype of q (dtype codes %d and %d)", (int)out->dtype,
+                        (int)q->dtype);
         if (!same_dims(out, q))
             return fail(FA_ERR_SHAPE, "out must have the shape of q %s (got %s)", dims(q, false).c_str(),
                         dims(out, false).c_str());
@@ -169,8 +172,8 @@ int append_check_impl(const fa_tensor* k_new, const fa_tensor* v_new, int32_t ba
         if (t->rank < 0 || t->rank > 4)
             return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
     for (const fa_tensor* t : {k_new, v_new, k_cache, v_cache})
-        if (t->dtype != FA_DTYPE_BF16)
-            return fail(FA_ERR_DTYPE, "kv append takes bf16 k_new/v_new/k_cache/v_cache (dtype code %d)",
+        if (!is_elem16(t->dtype) || t->dtype != k_new->dtype)
+            return fail(FA_ERR_DTYPE, "kv append takes bf16 or f16 k_new/v_new/k_cache/v_cache of one dtype (dtype code %d)",
                         (int)t->dtype);
     if (k_new->rank != 3 || v_new->rank != 3 || k_cache->rank != 4 || v_cache->rank != 4)
         return fail(FA_ERR_RANK,
@@ -267,9 +270,9 @@ int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v
     for (const fa_tensor* t : {q, k, v})
         if (t->rank < 0 || t->rank > 4)
             return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
-    if (q->dtype != FA_DTYPE_BF16 || k->dtype != FA_DTYPE_BF16 || v->dtype != FA_DTYPE_BF16)
-        return fail(FA_ERR_DTYPE, "flash-attn takes bf16 q/k/v (dtype codes q: %d, k: %d, v: %d)", (int)q->dtype,
-                    (int)k->dtype, (int)v->dtype);
+    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(FA_ERR_DTYPE, "flash-attn takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
+                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
     if (q->rank != 4 || k->rank != 4 || v->rank != 4)
         return fail(FA_ERR_RANK, "flash-attn expects (batch, seqlen, heads, head_dim) tensors of rank 4 (q: %d, k: %d, v: %d)",
                     (int)q->rank, (int)k->rank, (int)v->rank);
@@ -299,7 +302,9 @@ int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v
     if (B * Sq * H >= INT32_MAX || B * Sk >= INT32_MAX || B >= INT32_MAX)
         return fail(FA_ERR_ARGUMENT, "batch * seqlen_q * heads and batch * seqlen_k must be below 2^31");
     if (out) {
-        if (out->dtype != FA_DTYPE_BF16) return fail(FA_ERR_DTYPE, "out must be bf16 (dtype code %d)", (int)out->dtype);
+        if (out->dtype != q->dtype)
+            return fail(FA_ERR_DTYPE, "out must have the dtype of q (dtype codes %d and %d)", (int)out->dtype,
+                        (int)q->dtype);
         if (!same_dims(out, q))
             return fail(FA_ERR_SHAPE, "out must have the shape of q %s (got %s)", dims(q, false).c_str(),
                         dims(out, false).c_str());
@@ -394,6 +399,7 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
     p.chunk = plan.chunk;
     p.max_chunks = plan.max_chunks;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
+    p.f16 = q->dtype == FA_DTYPE_F16 ? 1 : 0;
     p.padded = ex.padded;
     p.uniform_q = ex.uniform_q;
     p.uniform_k = ex.uniform_k;

@@ -16,7 +16,7 @@
 // read the same K/V head and every K/V tile staged in LDS serves all of them.
 // Each wave owns MR rows; the workgroup's WR waves share the K/V tiles.
 //
-// Per wave the scores are computed transposed, S^T = K Q^T, with bf16 MFMA
+// Per wave the scores are computed transposed, S^T = K Q^T, with bf16 (or fp16) MFMA
 // (32x32x16 when MR = 32, 16x16x32 when MR = 16): every lane then holds a
 // single query row, so row max / row sum are in-lane plus one or two
 // cross-lane steps, and the O^T = V^T P^T product takes P straight from the
@@ -26,8 +26,8 @@
 // V is transposed once while being staged into LDS.
 //
 // Online softmax in the log2 domain (scale * log2 e folded in, v_exp_f32),
-// fp32 accumulation, P rounded to bf16 for the PV product, output rounded to
-// bf16 (round to nearest even).  Keys past a tile's end are zero-filled in LDS
+// fp32 accumulation, P rounded to the input element type for the PV product,
+// output rounded to it (round to nearest even).  Keys past a tile's end are zero-filled in LDS
 // and masked, so stale or NaN memory is never read.
 //
 // Split-KV: when a sequence's keys are cut into several chunks, each item
@@ -48,33 +48,77 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kNegInf = -__builtin_huge_valf();
 
-template <int MR>
+// Element types of q/k/v/out: bf16 and IEEE binary16 (fp16), both 16-bit, so
+// every layout, copy and LDS pattern is shared; they differ in the MFMA
+// instructions, the fp32 -> 16-bit rounding (nearest even) and the packed dot
+// used for row sums.
+struct EBf16 {
+    typedef __bf16 e8 __attribute__((ext_vector_type(8)));
+    typedef __bf16 e2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(e8, a), __builtin_bit_cast(e8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(e8, a), __builtin_bit_cast(e8, b), c, 0, 0, 0);
+    }
+    // two floats -> two bf16 in one v_cvt_pk_bf16_f32
+    static __device__ __forceinline__ unsigned int pack2(float a, float b) {
+        const f32x2 v = {a, b};
+        return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, e2));
+    }
+    static __device__ __forceinline__ unsigned short one(float a) {
+        return __builtin_bit_cast(unsigned short, static_cast<__bf16>(a));
+    }
+    // acc + both halves of a packed pair (v_dot2_f32_bf16 with ones)
+    static __device__ __forceinline__ float sum2(unsigned int pp, float acc) {
+        const e2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(e2, pp), ones, acc, false);
+    }
+};
+struct EF16 {
+    typedef _Float16 e8 __attribute__((ext_vector_type(8)));
+    typedef _Float16 e2 __attribute__((ext_vector_type(2)));
+    static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(e8, a), __builtin_bit_cast(e8, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(e8, a), __builtin_bit_cast(e8, b), c, 0, 0, 0);
+    }
+    // two floats -> two fp16 in one v_cvt_pk_f16_f32
+    static __device__ __forceinline__ unsigned int pack2(float a, float b) {
+        const f32x2 v = {a, b};
+        return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, e2));
+    }
+    static __device__ __forceinline__ unsigned short one(float a) {
+        return __builtin_bit_cast(unsigned short, static_cast<_Float16>(a));
+    }
+    static __device__ __forceinline__ float sum2(unsigned int pp, float acc) {
+        const e2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+        return __builtin_amdgcn_fdot2(__builtin_bit_cast(e2, pp), ones, acc, false);
+    }
+};
+
+template <int MR, class E>
 struct Mfma;
-template <>
-struct Mfma<32> {
+template <class E>
+struct Mfma<32, E> {
     static constexpr int KSTEP = 16;  // contraction length per instruction
     static constexpr int NACC = 16;   // accumulators per lane
     typedef f32x16 acc_t;
-    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
+    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) { return E::mma32(a, b, c); }
 };
-template <>
-struct Mfma<16> {
+template <class E>
+struct Mfma<16, E> {
     static constexpr int KSTEP = 32;
     static constexpr int NACC = 4;
     typedef f32x4 acc_t;
-    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) {
-        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
-                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-    }
+    static __device__ __forceinline__ acc_t mma(u32x4 a, u32x4 b, acc_t c) { return E::mma16(a, b, c); }
 };
 
 __device__ __forceinline__ int ceil_div(int a, int b) { return (a + b - 1) / b; }
@@ -96,18 +140,6 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int d0, int D, bool
     return u32x4{w[0], w[1], w[2], w[3]};
 }
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ unsigned int pack_bf16x2(float a, float b) {
-    const f32x2 v = {a, b};
-    return __builtin_bit_cast(unsigned int, __builtin_convertvector(v, bf16x2));
-}
-
-__device__ __forceinline__ unsigned short to_bf16(float a) {
-    return __builtin_bit_cast(unsigned short, static_cast<__bf16>(a));
-}
 
 __device__ __forceinline__ float wave_max_xor(float x, int mask) {
     return fmaxf(x, __shfl_xor(x, mask, 64));
@@ -344,9 +376,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // 16-byte chunks of row r stored at position (chunk ^ swizzle(r)), so that the
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
-template <int DP, int MR, int WR, int BN, int NS>
+template <class E, int DP, int MR, int WR, int BN, int NS>
 __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
-    typedef Mfma<MR> M;
+    typedef Mfma<MR, E> M;
     typedef typename M::acc_t acc_t;
     constexpr int NT = 64 * WR;
     constexpr int R = MR * WR;
@@ -767,19 +799,17 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             const float nm = (m_run == kNegInf) ? 0.f : -m_run;
             float rs0 = 0.f, rs1 = 0.f;
             unsigned int pk[NU][SPU / 2];
-            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-            const bf16x2_t ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int e = 0; e < SPU; e += 2) {
                     const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e], c2, nm));
                     const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e + 1], c2, nm));
-                    const unsigned int pp = pack_bf16x2(p0, p1);
+                    const unsigned int pp = E::pack2(p0, p1);
                     pk[u][e / 2] = pp;
                     // row sum of the bf16-rounded probabilities that feed the PV product
-                    if ((e / 2) & 1) rs1 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, rs1, false);
-                    else rs0 = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pp), ones, rs0, false);
+                    if ((e / 2) & 1) rs1 = E::sum2(pp, rs1);
+                    else rs0 = E::sum2(pp, rs0);
                 }
             float rs = rs0 + rs1;
             if constexpr (MR == 32) {
@@ -873,12 +903,12 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                 const float x0 = o[db][v4] * inv, x1 = o[db][v4 + 1] * inv;
                 const float x2 = o[db][v4 + 2] * inv, x3 = o[db][v4 + 3] * inv;
                 if (vec) {
-                    *reinterpret_cast<u32x2*>(orow + d) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+                    *reinterpret_cast<u32x2*>(orow + d) = u32x2{E::pack2(x0, x1), E::pack2(x2, x3)};
                 } else {
                     const float xs[4] = {x0, x1, x2, x3};
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
-                        if (d + j < D) orow[d + j] = to_bf16(xs[j]);
+                        if (d + j < D) orow[d + j] = E::one(xs[j]);
                 }
             }
         if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.lse_sh + tq + (int64_t)it.b * p.lse_bx] = lse2 * 0.6931471805599453f;
@@ -886,7 +916,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
 }
 
 // Merge split partials: one wave per (token, head).
-template <int DP>
+template <class E, int DP>
 __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int lane = threadIdx.x & 63;
     const int t = blockIdx.x;
@@ -927,44 +957,64 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         const int d = j * 64 + lane;
-        if (d < D) orow[d] = to_bf16(acc[j] * inv);
+        if (d < D) orow[d] = E::one(acc[j] * inv);
     }
     if (lse && lane == 0) *lse = (M + __builtin_amdgcn_logf(wsum)) * 0.6931471805599453f;
 }
 
 hipError_t g_last = hipSuccess;
 
-template <int DP, int MR, int WR, int BN, int NS>
+template <class E, int DP, int MR, int WR, int BN, int NS>
 hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
     // one workgroup per (item, K/V head) unit, padded to whole runs on all 8 XCDs
     const int64_t units = plan.items_bound * (int64_t)p.Hk;
     const int64_t run = 8 * (int64_t)p.xcd_chunk;
     dim3 grid((unsigned)((units + run - 1) / run * run));
-    hipLaunchKernelGGL((attn_fwd_kernel<DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
+    hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
     return hipGetLastError();
 }
 
-template <int DP>
+template <class E, int DP>
 hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
     dim3 grid((unsigned)p.total_q, (unsigned)((p.H + 3) / 4));
-    hipLaunchKernelGGL((combine_kernel<DP>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((combine_kernel<E, DP>), grid, dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
-template <int DP>
+template <class E, int DP>
 hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
     // one LDS stage here too: it frees registers and LDS for 3 resident workgroups
     // per CU, which beat a prefetching second stage (+6-8% on long prefill)
     if (plan.kind == KIND_PREFILL) {
-        if constexpr (DP <= 128) return launch_attn<DP, 32, 4, 64, 1>(plan, p, s);
-        else if constexpr (DP == 256) return launch_attn<DP, 32, 4, 32, 2>(plan, p, s);
-        else return launch_attn<DP, 16, 4, 32, 2>(plan, p, s);
+        if constexpr (DP <= 128) return launch_attn<E, DP, 32, 4, 64, 1>(plan, p, s);
+        else if constexpr (DP == 256) return launch_attn<E, DP, 32, 4, 32, 2>(plan, p, s);
+        else return launch_attn<E, DP, 16, 4, 32, 2>(plan, p, s);
     }
     // decode: 16 rows per wave, keys split over work items, one LDS stage: HBM
     // latency is hidden by the number of resident workgroups (LDS-limited),
     // which beats deeper per-wave pipelines on this path
-    if (plan.wr == 1) return launch_attn<DP, 16, 1, 32, 1>(plan, p, s);
-    return launch_attn<DP, 16, 4, 32, 1>(plan, p, s);
+    if (plan.wr == 1) return launch_attn<E, DP, 16, 1, 32, 1>(plan, p, s);
+    return launch_attn<E, DP, 16, 4, 32, 1>(plan, p, s);
+}
+
+template <class E>
+hipError_t launch_main(const Plan& plan, const FwdParams& p, hipStream_t s) {
+    switch (plan.dp) {
+        case 64: return launch_dp<E, 64>(plan, p, s);
+        case 128: return launch_dp<E, 128>(plan, p, s);
+        case 256: return launch_dp<E, 256>(plan, p, s);
+        default: return launch_dp<E, 512>(plan, p, s);
+    }
+}
+
+template <class E>
+hipError_t launch_merge(const Plan& plan, const FwdParams& p, hipStream_t s) {
+    switch (plan.dp) {
+        case 64: return launch_combine<E, 64>(p, s);
+        case 128: return launch_combine<E, 128>(p, s);
+        case 256: return launch_combine<E, 256>(p, s);
+        default: return launch_combine<E, 512>(p, s);
+    }
 }
 
 int env_int(const char* name, int dflt) {
@@ -1069,23 +1119,10 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
     e = hipGetLastError();
     if (e == hipSuccess && ev_start) e = hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
-    if (e == hipSuccess) {
-        switch (plan.dp) {
-            case 64: e = launch_dp<64>(plan, p, s); break;
-            case 128: e = launch_dp<128>(plan, p, s); break;
-            case 256: e = launch_dp<256>(plan, p, s); break;
-            default: e = launch_dp<512>(plan, p, s); break;
-        }
-    }
+    if (e == hipSuccess) e = p.f16 ? launch_main<EF16>(plan, p, s) : launch_main<EBf16>(plan, p, s);
     if (e == hipSuccess && ev_stop) e = hipEventRecord(static_cast<hipEvent_t>(ev_stop), s);
-    if (e == hipSuccess && plan.max_chunks > 1) {
-        switch (plan.dp) {
-            case 64: e = launch_combine<64>(p, s); break;
-            case 128: e = launch_combine<128>(p, s); break;
-            case 256: e = launch_combine<256>(p, s); break;
-            default: e = launch_combine<512>(p, s); break;
-        }
-    }
+    if (e == hipSuccess && plan.max_chunks > 1)
+        e = p.f16 ? launch_merge<EF16>(plan, p, s) : launch_merge<EBf16>(plan, p, s);
     g_last = e;
     return e == hipSuccess ? 0 : FA_ERR_HIP;
 }

@@ -9,7 +9,7 @@ namespace fa {
 
 // Everything a kernel launch needs.  Strides are in elements.
 struct FwdParams {
-    const uint16_t* q;      // bf16 bits
+    const uint16_t* q;      // bf16 or fp16 bits
     const uint16_t* k;
     const uint16_t* v;
     uint16_t* out;
@@ -38,6 +38,7 @@ struct FwdParams {
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t* tok_nc;        // [total_q] chunks of each token's sequence (split only)
+    int32_t f16;            // element type of q/k/v/out: 0 = bf16, 1 = fp16
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
     int32_t fast_copy;      // 1 = interior K/V tiles may use uniform-base + lane-offset copies
     int32_t k_rowb, v_rowb; // bytes between consecutive key rows (paged: slot stride; packed: token stride)

@@ -317,19 +317,19 @@ PADDED = {
 }
 
 
-def append_config(name: str, seed: Optional[int] = None) -> Workload:
+def append_config(name: str, seed: Optional[int] = None, dtype: str = "bf16") -> Workload:
     """Paged workload whose last ``lens_q[b]`` keys per sequence are the tokens an
     append writes.  Paged configs are used as they are; the long-prefill config
     (non-paged) gets a page-64 pool holding its whole sequences (Lq = Lk), and
     its ``q`` has num_heads_k heads (the new K rows' shape)."""
     cfg = CONFIGS[name]
     if cfg["page"] > 0:
-        return make_config(name, seed)
+        return make_config(name, seed, dtype=dtype)
     seed = DEFAULT_SEEDS[name] if seed is None else seed
     rng = np.random.Generator(np.random.PCG64(seed))
     lens_q, lens_k = lengths_for(name, rng)
     wl = make_custom(lens_q, lens_k, cfg["num_heads_k"], cfg["num_heads_k"], cfg["head_dim"], seed=seed,
-                     page=64, rng=rng, name=name + "-paged")
+                     page=64, rng=rng, name=name + "-paged", dtype=dtype)
     wl.extra["desc"] = cfg["desc"].replace("non-paged", "paged (P64)")
     return wl
 
