@@ -43,7 +43,8 @@ def _load():
         P = ctypes.c_void_p
         f.argtypes = [P, ctypes.c_int64, ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int64,
                       ctypes.c_int, ctypes.c_int, P, P, ctypes.c_int, P, ctypes.c_int,
-                      ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int]
+                      ctypes.c_double, ctypes.c_int, ctypes.c_int, P, P, P, ctypes.c_int, ctypes.c_int,
+                      P, ctypes.c_int64]
         f.restype = ctypes.c_int
         w = lib.fa_oracle_widen
         w.argtypes = [P, ctypes.c_int64, ctypes.c_int, P]
@@ -93,14 +94,16 @@ def default_threads() -> int:
 
 def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None, page_block_size: int = 0,
               softmax_scale: float = 1.0, window_left: int = -1, window_right: int = -1,
-              token_sel: Optional[np.ndarray] = None, nthreads: Optional[int] = None
-              ) -> Tuple[np.ndarray, np.ndarray]:
+              token_sel: Optional[np.ndarray] = None, nthreads: Optional[int] = None,
+              alibi_slopes=None) -> Tuple[np.ndarray, np.ndarray]:
     """fp64 attention over host bf16 or fp16 inputs (q, k, v of one element type).
 
     q: (total_q, H, D); k, v: (total_k, Hk, D) or, with ``block_table``,
     (num_blocks, page_block_size, Hk, D).  Returns ``out`` (total_q, H, D) float64
     and ``lse`` (H, total_q) float64 (natural log).  Rows not selected by
-    ``token_sel`` are returned as NaN.
+    ``token_sel`` are returned as NaN.  ``alibi_slopes``: None, (H,) or (batch, H)
+    slopes; key j of query row i then gets -slope * |i + Lk - Lq - j| added to its
+    scaled score.
     """
     lib = _load()
     qb, kb, vb = _bits(q), _bits(k), _bits(v)
@@ -125,6 +128,11 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None, page_block_
     if token_sel is not None:
         sel = np.ascontiguousarray(token_sel, dtype=np.uint8)
         assert sel.shape == (total_q,)
+    al, al_sb = None, 0
+    if alibi_slopes is not None:
+        al = np.ascontiguousarray(np.asarray(alibi_slopes, dtype=np.float64))
+        assert al.shape in ((H,), (batch, H)), al.shape
+        al_sb = H if al.ndim == 2 else 0
     dt = _dtype_of(q)
     assert _dtype_of(k) == dt and _dtype_of(v) == dt, "q, k and v must share one element type"
     rc = lib.fa_oracle_attention_t(qb.ctypes.data, total_q, H, D, kb.ctypes.data, vb.ctypes.data,
@@ -132,7 +140,8 @@ def attention(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None, page_block_
                                    bt_ptr, width, float(softmax_scale), int(window_left),
                                    int(window_right), None if sel is None else sel.ctypes.data,
                                    out.ctypes.data, lse.ctypes.data,
-                                   int(nthreads or default_threads()), DTYPES[dt])
+                                   int(nthreads or default_threads()), DTYPES[dt],
+                                   None if al is None else al.ctypes.data, al_sb)
     if rc != 0:
         raise ValueError("oracle rejected its arguments (code %d)" % rc)
     return out, lse
@@ -146,11 +155,11 @@ def widen(bits, dtype: str) -> np.ndarray:
     return out
 
 
-def attention_workload(wl, token_sel=None, nthreads=None):
+def attention_workload(wl, token_sel=None, nthreads=None, alibi_slopes=None):
     """Convenience: run the oracle on an object with the workload fields."""
     return attention(wl.q, wl.k, wl.v, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.block_table,
                      wl.page_block_size, wl.softmax_scale, wl.window_left, wl.window_right,
-                     token_sel=token_sel, nthreads=nthreads)
+                     token_sel=token_sel, nthreads=nthreads, alibi_slopes=alibi_slopes)
 
 
 def attention_padded(q, k, v, softmax_scale: float = 1.0, window_left: int = -1, window_right: int = -1,

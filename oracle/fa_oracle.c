@@ -13,7 +13,12 @@
  *   key j is visible to it iff 0 <= j < Lk and
  *       (window_left  < 0 or j >= a - window_left) and
  *       (window_right < 0 or j <= a + window_right).
- *   s_j = scale * sum_d q[i][h][d] * k_b[j][hk][d]
+ *   s_j = scale * sum_d q[i][h][d] * k_b[j][hk][d]  -  slope_bh * |a - j|
+ *         (the ALiBi term only when slopes are given; slope_bh = alibi[b][h] or
+ *         alibi[h]: the pages name the alibi_slopes argument through its shape
+ *         error, page "page_block_size ... does not match k shape", Related
+ *         errors; the linear distance penalty is the plainest reading, taken
+ *         with the same bottom-right alignment a as the window)
  *   out[i][h][:] = sum_j softmax(s)_j * v_b[j][hk][:]   (0 if no key is visible)
  *   lse[h][i]    = log(sum_j exp(s_j))                  (-inf if no key is visible)
  *
@@ -84,6 +89,8 @@ typedef struct {
     const int32_t *block_table;
     int bt_width;
     double scale;
+    const double *alibi;   /* NULL, or slopes: alibi[b * alibi_sb + h] */
+    int64_t alibi_sb;
     int window_left, window_right;
     const uint8_t *token_sel;
     double *out, *lse;
@@ -145,6 +152,7 @@ static void run_item(job_t *J, int b, int h, double *s, int64_t *koff) {
             else
                 for (int d = 0; d < D; ++d) dot += bf16_to_double(qrow[d]) * bf16_to_double(krow[d]);
             s[j] = J->scale * dot;
+            if (J->alibi) s[j] -= J->alibi[(int64_t)b * J->alibi_sb + h] * fabs((double)(i + Lk - Lq - j));
             if (s[j] > m) m = s[j];
             ++n_visible;
         }
@@ -199,6 +207,8 @@ static void *worker(void *arg) {
  *   block_table [batch][bt_width] int32 (page > 0 only)
  *   token_sel   [total_q] or NULL: rows with 0 are skipped (left untouched)
  *   out  [total_q][num_heads][head_dim] double;  lse [num_heads][total_q] double
+ *   alibi  NULL or ALiBi slopes, slope of (sequence b, head h) at alibi[b * alibi_sb + h]
+ *          (alibi_sb = 0: one slope per head for every sequence)
  * Returns 0, or -1 for bad arguments, -2 for a block id / row outside the pool,
  * -3 when memory runs out.
  */
@@ -207,7 +217,8 @@ int fa_oracle_attention_t(const uint16_t *q, int64_t total_q, int num_heads, int
                           int num_heads_k, const int32_t *cu_q, const int32_t *cu_k, int batch,
                           const int32_t *block_table, int bt_width, double scale,
                           int window_left, int window_right, const uint8_t *token_sel,
-                          double *out, double *lse, int nthreads, int dtype) {
+                          double *out, double *lse, int nthreads, int dtype,
+                          const double *alibi, int64_t alibi_sb) {
     if (num_heads <= 0 || num_heads_k <= 0 || head_dim <= 0 || batch < 0) return -1;
     if (num_heads % num_heads_k != 0) return -1;
     if (page < 0 || (page > 0 && !block_table)) return -1;
@@ -222,6 +233,7 @@ int fa_oracle_attention_t(const uint16_t *q, int64_t total_q, int num_heads, int
     J.kv_rows = kv_rows; J.page = page; J.cu_q = cu_q; J.cu_k = cu_k; J.batch = batch;
     J.block_table = block_table; J.bt_width = bt_width; J.scale = scale;
     J.window_left = window_left; J.window_right = window_right; J.token_sel = token_sel;
+    J.alibi = alibi; J.alibi_sb = alibi_sb;
     J.out = out; J.lse = lse;
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;
@@ -245,7 +257,7 @@ int fa_oracle_attention(const uint16_t *q, int64_t total_q, int num_heads, int h
                         double *out, double *lse, int nthreads) {
     return fa_oracle_attention_t(q, total_q, num_heads, head_dim, k, v, kv_rows, page, num_heads_k, cu_q,
                                  cu_k, batch, block_table, bt_width, scale, window_left, window_right,
-                                 token_sel, out, lse, nthreads, 0);
+                                 token_sel, out, lse, nthreads, 0, NULL, 0);
 }
 
 /*

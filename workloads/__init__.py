@@ -32,6 +32,7 @@ import torch
 
 __all__ = [
     "Workload", "CONFIGS", "make_config", "make_custom", "make_append", "append_config", "make_padded",
+    "alibi_slopes",
     "PADDED", "normal_bf16",
     "lengths_for", "C4_TOTAL",
 ]
@@ -286,6 +287,19 @@ def make_append(lens_new: Sequence[int], lens_k: Sequence[int], num_heads_k: int
                      spare=spare, rng=rng, seed=seed, name="append")
     v_new = normal_bf16(rng, tuple(wl.q.shape))
     return wl, wl.q, v_new, wl.cu_seqlens_q
+
+
+def alibi_slopes(num_heads: int, batch: int = 0, seed: Optional[int] = None) -> np.ndarray:
+    """ALiBi slopes as float32: (num_heads,), or (batch, num_heads) when batch > 0.
+    Without a seed, the geometric sequence 2^(-8 h / num_heads), h = 1..num_heads, of
+    the ALiBi paper (Press et al., 2022); with a seed, uniform draws in [0, 1)."""
+    if seed is None:
+        s = 2.0 ** (-8.0 * np.arange(1, num_heads + 1) / num_heads)
+        out = np.tile(s, (batch, 1)) if batch > 0 else s
+    else:
+        rng = np.random.Generator(np.random.PCG64(seed))
+        out = rng.random((batch, num_heads) if batch > 0 else (num_heads,))
+    return np.ascontiguousarray(out, dtype=np.float32)
 
 
 def make_padded(B: int, Sq: int, Sk: int, num_heads: int, num_heads_k: int, head_dim: int, *,
