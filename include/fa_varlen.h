@@ -53,7 +53,7 @@ extern "C" {
  * all IEEE binary16 (fp16) -- the candle wrapper is generic over the element
  * type (page "flash-attn-varlen paged expects k/v tensors of rank 4", Source);
  * block tables are int32 */
-enum fa_dtype { FA_DTYPE_BF16 = 1, FA_DTYPE_I32 = 2, FA_DTYPE_F16 = 3 };
+enum fa_dtype { FA_DTYPE_BF16 = 1, FA_DTYPE_I32 = 2, FA_DTYPE_F16 = 3, FA_DTYPE_F32 = 4 };
 
 /* status codes */
 enum fa_status {
@@ -95,11 +95,15 @@ typedef struct fa_tensor {
  *   block_table  NULL = non-paged; else int32 (batch, max_blocks_per_seq), last dim contiguous
  *   page_block_size  0 = not given; must equal k.shape[1] and be a multiple of 32 when paged;
  *                ignored without a block table
+ *   alibi_slopes NULL, or fp32 (num_heads) or (batch, num_heads), last dim contiguous
+ *                (the shape the pages' "shape mismatch alibi_slopes {:?}, expected {:?}"
+ *                error guards: page "page_block_size ... does not match k shape",
+ *                Related errors)
  * Returns FA_OK or the first failing check's code (text in fa_last_error()).
  */
 int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                     const fa_tensor* out, int32_t batch, const fa_tensor* block_table,
-                    int32_t page_block_size);
+                    int32_t page_block_size, const fa_tensor* alibi_slopes);
 
 /*
  * fa_varlen_workspace_bytes -- device scratch that fa_varlen_fwd needs for the
@@ -128,6 +132,9 @@ int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_t
  *       window_left >= 0) and j <= a + window_right (when window_right >= 0).
  *       Negative = unbounded; causal is (-1, 0).  Query head h reads key/value
  *       head h / (num_heads / num_heads_k).  A row that sees no key gets out = 0.
+ *   alibi_slopes  NULL, or device fp32 slopes as for fa_varlen_check: the scaled
+ *       score of key j for query row i of head h gets -slope * |a - j| added
+ *       (slope = alibi[h], or alibi[b][h] for per-sequence slopes).
  *   softmax_lse  NULL, or device fp32 [num_heads][total_q]: natural-log
  *       sum of exp of the scaled scores per row (-inf for a row that sees no key).
  *   workspace, workspace_bytes  device scratch of at least
@@ -138,8 +145,8 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                   const fa_tensor* out, const int32_t* cu_seqlens_q,
                   const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
                   int32_t page_block_size, float softmax_scale, int32_t window_left,
-                  int32_t window_right, float* softmax_lse, void* workspace,
-                  size_t workspace_bytes, void* stream);
+                  int32_t window_right, const fa_tensor* alibi_slopes, float* softmax_lse,
+                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Padded (non-varlen) entry: the same forward over batch-major tensors in which
@@ -155,20 +162,23 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
  *            tensor viewed as (B, S, H, D)).
  *   k, v     (B, Sk, Hk, D), last dim contiguous, same shape; H % Hk == 0;
  *            1 <= D <= 512; B*Sq*H and B*Sk below 2^31.
- *   softmax_scale, window_left, window_right  as for fa_varlen_fwd (query row i
- *            sits at key position i + Sk - Sq).
+ *   softmax_scale, window_left, window_right, alibi_slopes  as for
+ *            fa_varlen_fwd (query row i sits at key position i + Sk - Sq; per-
+ *            sequence slopes are (B, H)).
  *   softmax_lse  NULL or device fp32 (B, H, Sq), natural log.
  *   workspace    at least fa_padded_workspace_bytes() bytes (may be NULL if 0).
  * Errors, ownership and asynchrony as for fa_varlen_fwd; fa_padded_check runs
  * the contract alone without a GPU.
  */
-int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out);
+int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                    const fa_tensor* alibi_slopes);
 
 int fa_padded_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, size_t* bytes);
 
 int fa_padded_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-                  float softmax_scale, int32_t window_left, int32_t window_right, float* softmax_lse,
-                  void* workspace, size_t workspace_bytes, void* stream);
+                  float softmax_scale, int32_t window_left, int32_t window_right,
+                  const fa_tensor* alibi_slopes, float* softmax_lse, void* workspace,
+                  size_t workspace_bytes, void* stream);
 
 /*
  * fa_kv_append_check -- the contract of fa_kv_append alone (host code, no GPU

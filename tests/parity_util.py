@@ -7,7 +7,14 @@ import varlen_flash_attention_fa_amd as fa
 
 MAX_ABS = 2e-2     # bf16 output vs fp64 oracle, worst element
 MEAN_ABS = 2e-3    # mean over all compared elements
-LSE_ABS = 2e-3     # natural-log sum-exp, fp32 vs fp64
+# natural-log sum-exp, fp32 vs fp64.  The kernel's row sum adds the probabilities
+# after their rounding to the 16-bit type that feeds the PV product (so out is
+# normalised by exactly the weights it used); one round-to-nearest bf16 value is
+# off by at most 2^-8 of itself, so the sum of non-negative terms is too and
+# |d lse| <= -ln(1 - 2^-8) = 3.92e-3, plus fp32 rounding of the scores.  When many
+# comparable terms share a row the errors average out; when one term dominates
+# (ALiBi's distance penalty) the bound is nearly reached.
+LSE_ABS = 4e-3
 
 
 def to_dev(wl, dev="cuda"):
@@ -49,5 +56,6 @@ def assert_close(out_gpu, lse_gpu, ref_out, ref_lse, rows=None, what=""):
         assert np.array_equal(np.isfinite(l), fin), what + ": lse finiteness differs"
         assert np.all(l[~fin] == ref_lse[~fin]), what + ": lse of empty rows"
         if fin.any():
-            assert np.abs(l[fin] - ref_lse[fin]).max() <= LSE_ABS, what + ": lse"
+            le = np.abs(l[fin] - ref_lse[fin])
+            assert le.max() <= LSE_ABS, "%s: lse max|d|=%.3g mean|d|=%.3g" % (what, le.max(), le.mean())
     return err

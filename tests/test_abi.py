@@ -356,3 +356,26 @@ def test_f16_accepted_and_dtypes_must_match(lib):
     qp, kp = desc([2, 5, 4, 64], dtype=FA_DTYPE_F16), desc([2, 9, 2, 64], dtype=FA_DTYPE_F16)
     assert pcheck(q=qp, k=kp, v=kp)[0] == 0
     assert pcheck(q=qp)[0] == code["FA_ERR_DTYPE"]
+
+
+def test_alibi_slopes_contract(lib):
+    from varlen_flash_attention_fa_amd import FA_DTYPE_F32
+    code, t, _ = tmpl("shape mismatch alibi_slopes")
+    ok1 = desc([4], dtype=FA_DTYPE_F32)
+    ok2 = desc([3, 4], dtype=FA_DTYPE_F32)
+    assert fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0, ok1) == 0
+    assert fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0, ok2) == 0
+    rc = fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0, desc([8], dtype=FA_DTYPE_F32))
+    assert rc == code and fa.fa_last_error() == render(t, _seq=[dl([8]), dl([4])])
+    rc = fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0, desc([2, 4], dtype=FA_DTYPE_F32))
+    assert rc == code and fa.fa_last_error() == render(t, _seq=[dl([2, 4]), dl([3, 4])])
+    codes = {v: k for k, v in fa.STATUS.items()}
+    assert fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0, desc([4])) == codes["FA_ERR_DTYPE"]
+    assert fa.fa_varlen_check(Q, K3, K3, None, 3, None, 0,
+                              desc([3, 4], stride=[8, 2], dtype=FA_DTYPE_F32)) == codes["FA_ERR_CONTIGUOUS"]
+    # the earlier checks come first
+    assert fa.fa_varlen_check(desc([86, 4]), K3, K3, None, 3, None, 0, desc([8])) == codes["FA_ERR_RANK"]
+    # padded: (H) or (B, H)
+    assert fa.fa_padded_check(QP, KP4, KP4, None, ok1) == 0
+    assert fa.fa_padded_check(QP, KP4, KP4, None, desc([2, 4], dtype=FA_DTYPE_F32)) == 0
+    assert fa.fa_padded_check(QP, KP4, KP4, None, desc([3, 4], dtype=FA_DTYPE_F32)) == code

@@ -23,7 +23,7 @@ __all__ = [
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
     "fa_varlen_set_kernel_events", "fa_kv_append_check", "fa_kv_append", "kv_append",
     "fa_padded_check", "fa_padded_workspace_bytes", "fa_padded_fwd", "padded_fwd",
-    "FA_DTYPE_BF16", "FA_DTYPE_I32", "FA_DTYPE_F16", "STATUS",
+    "FA_DTYPE_BF16", "FA_DTYPE_I32", "FA_DTYPE_F16", "FA_DTYPE_F32", "STATUS",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -32,6 +32,7 @@ _LIB_PATH = os.path.join(_HERE, "libfa_varlen.so")
 FA_DTYPE_BF16 = 1
 FA_DTYPE_I32 = 2
 FA_DTYPE_F16 = 3
+FA_DTYPE_F32 = 4
 STATUS = {0: "FA_OK", 1: "FA_ERR_RANK", 2: "FA_ERR_CONTIGUOUS", 3: "FA_ERR_SHAPE",
           4: "FA_ERR_PAGE_SIZE", 5: "FA_ERR_HEAD_DIM", 6: "FA_ERR_DTYPE", 7: "FA_ERR_ARGUMENT",
           8: "FA_ERR_WORKSPACE", 9: "FA_ERR_DEVICE", 10: "FA_ERR_HIP"}
@@ -68,23 +69,23 @@ def load():
                            "(or __graft_entry__.build())")
     lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.POINTER(FaTensor)
-    lib.fa_varlen_check.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_int32]
+    lib.fa_varlen_check.argtypes = [P, P, P, P, ctypes.c_int32, P, ctypes.c_int32, P]
     lib.fa_varlen_check.restype = ctypes.c_int
     lib.fa_varlen_workspace_bytes.argtypes = [P, P, P, ctypes.c_int32, P, ctypes.c_int32,
                                               ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_varlen_workspace_bytes.restype = ctypes.c_int
     lib.fa_varlen_fwd.argtypes = [P, P, P, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, P,
-                                  ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, P,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_varlen_fwd.restype = ctypes.c_int
     lib.fa_varlen_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_varlen_set_kernel_events.restype = ctypes.c_int
-    lib.fa_padded_check.argtypes = [P, P, P, P]
+    lib.fa_padded_check.argtypes = [P, P, P, P, P]
     lib.fa_padded_check.restype = ctypes.c_int
     lib.fa_padded_workspace_bytes.argtypes = [P, P, P, ctypes.POINTER(ctypes.c_size_t)]
     lib.fa_padded_workspace_bytes.restype = ctypes.c_int
-    lib.fa_padded_fwd.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
-                                  ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    lib.fa_padded_fwd.argtypes = [P, P, P, P, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, P,
+                                  ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_padded_fwd.restype = ctypes.c_int
     lib.fa_kv_append_check.argtypes = [P, P, ctypes.c_int32, P, P, P, ctypes.c_int32]
     lib.fa_kv_append_check.restype = ctypes.c_int
@@ -118,7 +119,8 @@ def desc(shape: Sequence[int], stride: Optional[Sequence[int]] = None, dtype: in
 
 def _tdesc(t) -> FaTensor:
     import torch
-    dt = {torch.bfloat16: FA_DTYPE_BF16, torch.int32: FA_DTYPE_I32, torch.float16: FA_DTYPE_F16}.get(t.dtype, 0)
+    dt = {torch.bfloat16: FA_DTYPE_BF16, torch.int32: FA_DTYPE_I32, torch.float16: FA_DTYPE_F16,
+          torch.float32: FA_DTYPE_F32}.get(t.dtype, 0)
     return desc(list(t.shape), list(t.stride()), dt, t.data_ptr())
 
 
@@ -136,10 +138,11 @@ def _raise_on(rc: int) -> None:
 
 
 def fa_varlen_check(q: FaTensor, k: FaTensor, v: FaTensor, out: Optional[FaTensor], batch: int,
-                    block_table: Optional[FaTensor], page_block_size: int) -> int:
+                    block_table: Optional[FaTensor], page_block_size: int,
+                    alibi_slopes: Optional[FaTensor] = None) -> int:
     """Shape/stride/dtype contract only (host code, no GPU needed).  Returns the status."""
     return load().fa_varlen_check(_ref(q), _ref(k), _ref(v), _ref(out), int(batch),
-                                  _ref(block_table), int(page_block_size or 0))
+                                  _ref(block_table), int(page_block_size or 0), _ref(alibi_slopes))
 
 
 def fa_varlen_workspace_bytes(q: FaTensor, k: FaTensor, v: FaTensor, batch: int,
@@ -154,13 +157,14 @@ def fa_varlen_workspace_bytes(q: FaTensor, k: FaTensor, v: FaTensor, batch: int,
 def fa_varlen_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqlens_q: int,
                   cu_seqlens_k: int, batch: int, block_table: Optional[FaTensor],
                   page_block_size: int, softmax_scale: float, window_left: int, window_right: int,
-                  softmax_lse: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+                  softmax_lse: int, workspace: int, workspace_bytes: int, stream: int,
+                  alibi_slopes: Optional[FaTensor] = None) -> int:
     """Raw C-ABI call with descriptors and integer device addresses.  Returns the status."""
     return load().fa_varlen_fwd(_ref(q), _ref(k), _ref(v), _ref(out), cu_seqlens_q or None,
                                 cu_seqlens_k or None, int(batch), _ref(block_table),
                                 int(page_block_size or 0), float(softmax_scale), int(window_left),
-                                int(window_right), softmax_lse or None, workspace or None,
-                                int(workspace_bytes), stream or None)
+                                int(window_right), _ref(alibi_slopes), softmax_lse or None,
+                                workspace or None, int(workspace_bytes), stream or None)
 
 
 def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:
@@ -168,9 +172,10 @@ def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:
     return load().fa_varlen_set_kernel_events(start_event or None, stop_event or None)
 
 
-def fa_padded_check(q: FaTensor, k: FaTensor, v: FaTensor, out: Optional[FaTensor]) -> int:
+def fa_padded_check(q: FaTensor, k: FaTensor, v: FaTensor, out: Optional[FaTensor],
+                    alibi_slopes: Optional[FaTensor] = None) -> int:
     """Contract of the padded entry only (host code, no GPU needed).  Returns the status."""
-    return load().fa_padded_check(_ref(q), _ref(k), _ref(v), _ref(out))
+    return load().fa_padded_check(_ref(q), _ref(k), _ref(v), _ref(out), _ref(alibi_slopes))
 
 
 def fa_padded_workspace_bytes(q: FaTensor, k: FaTensor, v: FaTensor) -> int:
@@ -181,15 +186,16 @@ def fa_padded_workspace_bytes(q: FaTensor, k: FaTensor, v: FaTensor) -> int:
 
 def fa_padded_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, softmax_scale: float,
                   window_left: int, window_right: int, softmax_lse: int, workspace: int,
-                  workspace_bytes: int, stream: int) -> int:
+                  workspace_bytes: int, stream: int, alibi_slopes: Optional[FaTensor] = None) -> int:
     """Raw C-ABI call of the padded entry.  Returns the status."""
     return load().fa_padded_fwd(_ref(q), _ref(k), _ref(v), _ref(out), float(softmax_scale), int(window_left),
-                                int(window_right), softmax_lse or None, workspace or None,
+                                int(window_right), _ref(alibi_slopes), softmax_lse or None, workspace or None,
                                 int(workspace_bytes), stream or None)
 
 
 def padded_fwd(q, k, v, softmax_scale: Optional[float] = None, window_left: int = -1,
-               window_right: int = -1, return_lse: bool = False, out=None, workspace=None, stream=None):
+               window_right: int = -1, return_lse: bool = False, out=None, workspace=None, stream=None,
+               alibi_slopes=None):
     """Forward over padded (B, Sq, H, D) / (B, Sk, Hk, D) device tensors.
 
     Returns ``out`` (B, Sq, H, D) bf16, plus ``lse`` (B, H, Sq) fp32 if ``return_lse``.
@@ -201,7 +207,8 @@ def padded_fwd(q, k, v, softmax_scale: Optional[float] = None, window_left: int 
     if out is None:
         out = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     dout = _tdesc(out)
-    _raise_on(fa_padded_check(dq, dk, dv, dout))
+    dal = _tdesc(alibi_slopes) if alibi_slopes is not None else None
+    _raise_on(fa_padded_check(dq, dk, dv, dout, dal))
     nbytes = fa_padded_workspace_bytes(dq, dk, dv)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
@@ -213,7 +220,7 @@ def padded_fwd(q, k, v, softmax_scale: Optional[float] = None, window_left: int 
     _raise_on(fa_padded_fwd(dq, dk, dv, dout, softmax_scale, window_left, window_right,
                             lse.data_ptr() if lse is not None else 0,
                             workspace.data_ptr() if (nbytes and workspace is not None) else 0, nbytes,
-                            int(stream)))
+                            int(stream), dal))
     return (out, lse) if return_lse else out
 
 
@@ -263,7 +270,7 @@ def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_cache, 
 def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,
                page_block_size: Optional[int] = None, softmax_scale: Optional[float] = None,
                window_left: int = -1, window_right: int = -1, return_lse: bool = False,
-               out=None, workspace=None, stream=None):
+               out=None, workspace=None, stream=None, alibi_slopes=None):
     """Varlen flash-attention forward on device tensors.
 
     q (total_q, H, D) bf16 or fp16; k/v (total_k, Hk, D) or paged (num_blocks, P, Hk, D), q's dtype,
@@ -287,7 +294,8 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,
         out = torch.empty_like(q, memory_format=torch.contiguous_format) if q.dim() == 3 else \
             torch.empty(0, device=q.device, dtype=q.dtype)
     dout = _tdesc(out)
-    rc = fa_varlen_check(dq, dk, dv, dout, batch, dbt, page_block_size or 0)
+    dal = _tdesc(alibi_slopes) if alibi_slopes is not None else None
+    rc = fa_varlen_check(dq, dk, dv, dout, batch, dbt, page_block_size or 0, dal)
     _raise_on(rc)
     nbytes = fa_varlen_workspace_bytes(dq, dk, dv, batch, dbt, page_block_size or 0)
     if nbytes and (workspace is None or workspace.numel() * workspace.element_size() < nbytes):
@@ -301,6 +309,6 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,
                        dbt, page_block_size or 0, softmax_scale, window_left, window_right,
                        lse.data_ptr() if lse is not None else 0,
                        workspace.data_ptr() if (nbytes and workspace is not None) else 0,
-                       nbytes, int(stream))
+                       nbytes, int(stream), dal)
     _raise_on(rc)
     return (out, lse) if return_lse else out

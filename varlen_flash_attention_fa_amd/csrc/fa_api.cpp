@@ -57,8 +57,29 @@ bool same_dims(const fa_tensor* a, const fa_tensor* b) {
     return true;
 }
 
+// ALiBi slopes: fp32, (num_heads) or (batch, num_heads), last dim contiguous.  The
+// shape text is the one the pages list among the related errors (page
+// "page_block_size ... does not match k shape", Related errors).
+int alibi_check(const fa_tensor* al, int64_t batch, int64_t num_heads) {
+    if (!al) return FA_OK;
+    if (al->rank < 0 || al->rank > 4) return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)al->rank);
+    if (al->dtype != FA_DTYPE_F32)
+        return fail(FA_ERR_DTYPE, "alibi_slopes must be f32 (dtype code %d)", (int)al->dtype);
+    const bool ok1 = al->rank == 1 && al->shape[0] == num_heads;
+    const bool ok2 = al->rank == 2 && al->shape[0] == batch && al->shape[1] == num_heads;
+    if (!ok1 && !ok2) {
+        const std::string exp = al->rank == 2 ? "[" + std::to_string(batch) + ", " + std::to_string(num_heads) + "]"
+                                              : "[" + std::to_string(num_heads) + "]";
+        return fail(FA_ERR_SHAPE, "shape mismatch alibi_slopes %s, expected %s", dims(al, false).c_str(), exp.c_str());
+    }
+    if (al->stride[al->rank - 1] != 1 && al->shape[al->rank - 1] > 1)
+        return fail(FA_ERR_CONTIGUOUS, "alibi_slopes last dimension must be contiguous");
+    if (al->rank == 2 && al->stride[0] < 0) return fail(FA_ERR_SHAPE, "negative alibi_slopes stride");
+    return FA_OK;
+}
+
 int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-               int32_t batch, const fa_tensor* bt, int32_t page_block_size) {
+               int32_t batch, const fa_tensor* bt, int32_t page_block_size, const fa_tensor* alibi) {
     if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
     for (const fa_tensor* t : {q, k, v})
         if (t->rank < 0 || t->rank > 4)
@@ -157,7 +178,7 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
     } else if (k->shape[0] >= INT32_MAX) {
         return fail(FA_ERR_ARGUMENT, "total_k must be below 2^31");
     }
-    return FA_OK;
+    return alibi_check(alibi, batch, num_heads);
 }
 
 // Contract of the paged K/V append.  Its page and head-size rules are the ones
@@ -265,7 +286,8 @@ struct Extra {
 };
 
 // Contract of the padded (non-varlen) entry: q/out (B, Sq, H, D), k/v (B, Sk, Hk, D).
-int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out) {
+int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                      const fa_tensor* alibi) {
     if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
     for (const fa_tensor* t : {q, k, v})
         if (t->rank < 0 || t->rank > 4)
@@ -315,7 +337,7 @@ int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v
                 return fail(FA_ERR_SHAPE, "negative shape or stride %s / %s", dims(out, false).c_str(),
                             dims(out, true).c_str());
     }
-    return FA_OK;
+    return alibi_check(alibi, B, H);
 }
 
 fa::Shapes padded_shapes(const fa_tensor* q, const fa_tensor* k) {
@@ -336,7 +358,8 @@ fa::Shapes padded_shapes(const fa_tensor* q, const fa_tensor* k) {
 int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
             int32_t page_block_size, float softmax_scale, int32_t window_left, int32_t window_right,
-            float* softmax_lse, void* workspace, size_t workspace_bytes, void* stream, const Extra& ex) {
+            const fa_tensor* alibi, float* softmax_lse, void* workspace, size_t workspace_bytes, void* stream,
+            const Extra& ex) {
     const bool paged = block_table != nullptr;
     const int64_t total_q = q->shape[0];
     if (paged && (!block_table->data || !is_device_ptr(block_table->data)))
@@ -349,6 +372,8 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
     if (!out->data || !is_device_ptr(out->data)) return fail(FA_ERR_DEVICE, "out must be a cuda tensor");
     if (softmax_lse && !is_device_ptr(softmax_lse))
         return fail(FA_ERR_DEVICE, "softmax_lse must be a cuda tensor");
+    if (alibi && (!alibi->data || !is_device_ptr(alibi->data)))
+        return fail(FA_ERR_DEVICE, "alibi_slopes must be a cuda tensor");
 
     fa::Plan plan;
     int rc = fa::make_plan(ex.shapes, &plan);
@@ -400,6 +425,8 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
     p.max_chunks = plan.max_chunks;
     p.scale_log2 = softmax_scale * 1.4426950408889634f;
     p.f16 = q->dtype == FA_DTYPE_F16 ? 1 : 0;
+    p.alibi = alibi ? static_cast<const float*>(alibi->data) : nullptr;
+    p.alibi_sb = (alibi && alibi->rank == 2) ? alibi->stride[0] : 0;
     p.padded = ex.padded;
     p.uniform_q = ex.uniform_q;
     p.uniform_k = ex.uniform_k;
@@ -450,14 +477,15 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
 extern "C" {
 
 int fa_varlen_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-                    int32_t batch, const fa_tensor* block_table, int32_t page_block_size) {
-    return check_impl(q, k, v, out, batch, block_table, page_block_size);
+                    int32_t batch, const fa_tensor* block_table, int32_t page_block_size,
+                    const fa_tensor* alibi_slopes) {
+    return check_impl(q, k, v, out, batch, block_table, page_block_size, alibi_slopes);
 }
 
 int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, int32_t batch,
                               const fa_tensor* block_table, int32_t page_block_size, size_t* bytes) {
     if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
-    int rc = check_impl(q, k, v, nullptr, batch, block_table, page_block_size);
+    int rc = check_impl(q, k, v, nullptr, batch, block_table, page_block_size, nullptr);
     if (rc) return rc;
     fa::Plan plan;
     rc = fa::make_plan(shapes_of(q, k, batch, block_table, page_block_size), &plan);
@@ -469,10 +497,10 @@ int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_t
 int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
                   const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
                   const fa_tensor* block_table, int32_t page_block_size, float softmax_scale,
-                  int32_t window_left, int32_t window_right, float* softmax_lse, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  int32_t window_left, int32_t window_right, const fa_tensor* alibi_slopes,
+                  float* softmax_lse, void* workspace, size_t workspace_bytes, void* stream) {
     if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
-    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size);
+    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size, alibi_slopes);
     if (rc) return rc;
     if (batch == 0 || q->shape[0] == 0) return FA_OK;  // nothing to compute, nothing written
     if (!cu_seqlens_q || !is_device_ptr(cu_seqlens_q))
@@ -483,16 +511,17 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     ex.lse_sh = q->shape[0];
     ex.shapes = shapes_of(q, k, batch, block_table, page_block_size);
     return run_fwd(q, k, v, out, cu_seqlens_q, cu_seqlens_k, batch, block_table, page_block_size, softmax_scale,
-                   window_left, window_right, softmax_lse, workspace, workspace_bytes, stream, ex);
+                   window_left, window_right, alibi_slopes, softmax_lse, workspace, workspace_bytes, stream, ex);
 }
 
-int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out) {
-    return padded_check_impl(q, k, v, out);
+int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                    const fa_tensor* alibi_slopes) {
+    return padded_check_impl(q, k, v, out, alibi_slopes);
 }
 
 int fa_padded_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, size_t* bytes) {
     if (!bytes) return fail(FA_ERR_ARGUMENT, "bytes must not be NULL");
-    int rc = padded_check_impl(q, k, v, nullptr);
+    int rc = padded_check_impl(q, k, v, nullptr, nullptr);
     if (rc) return rc;
     fa::Plan plan;
     rc = fa::make_plan(padded_shapes(q, k), &plan);
@@ -502,10 +531,10 @@ int fa_padded_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_t
 }
 
 int fa_padded_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
-                  float softmax_scale, int32_t window_left, int32_t window_right, float* softmax_lse,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+                  float softmax_scale, int32_t window_left, int32_t window_right, const fa_tensor* alibi_slopes,
+                  float* softmax_lse, void* workspace, size_t workspace_bytes, void* stream) {
     if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
-    int rc = padded_check_impl(q, k, v, out);
+    int rc = padded_check_impl(q, k, v, out, alibi_slopes);
     if (rc) return rc;
     const int64_t B = q->shape[0], Sq = q->shape[1], Sk = k->shape[1];
     if (B == 0 || Sq == 0) return FA_OK;
@@ -541,7 +570,7 @@ int fa_padded_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
                 out->stride[0] % 8 == 0;
     ex.shapes = padded_shapes(q, k);
     return run_fwd(&q3, &k3, &v3, &o3, nullptr, nullptr, (int32_t)B, nullptr, 0, softmax_scale, window_left,
-                   window_right, softmax_lse, workspace, workspace_bytes, stream, ex);
+                   window_right, alibi_slopes, softmax_lse, workspace, workspace_bytes, stream, ex);
 }
 
 int fa_kv_append_check(const fa_tensor* k_new, const fa_tensor* v_new, int32_t batch,

@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // 16-byte chunks of row r stored at position (chunk ^ swizzle(r)), so that the
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
-template <class E, int DP, int MR, int WR, int BN, int NS>
+template <class E, int DP, int MR, int WR, int BN, int NS, bool AL>
 __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR, E> M;
     typedef typename M::acc_t acc_t;
@@ -490,6 +490,13 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             qreg[s] = x ^ u32x4{qflip, qflip, qflip, qflip};
         }
     }
+
+    // ALiBi (AL: the call has slopes; a separate instantiation so the plain
+    // kernel keeps its registers): this row's score for key n gets
+    // al2 * |apos - n| (log2 units)
+    float al2 = 0.f;
+    if constexpr (AL) al2 = row_ok ? -p.alibi[(int64_t)it.b * p.alibi_sb + h] * 1.4426950408889634f : 0.f;
+    const int apos = qi + Lk - Lq;
 
     acc_t o[NDB];
 #pragma unroll
@@ -758,7 +765,24 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                 }
             }
 
-            // ---- mask, running max (raw scores; c2 > 0 so the scaled max is c2 * max)
+            // ---- ALiBi (when slopes are given): scores become c2 * s + al2 * |apos - n|,
+            // already scaled, so the rest of the tile uses the factor cc = 1
+            float cc = c2;
+            if constexpr (AL) {
+#pragma unroll
+                for (int u = 0; u < NU; ++u)
+#pragma unroll
+                    for (int e = 0; e < SPU; ++e) {
+                        int key;
+                        if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
+                        else key = u * 32 + kgrp * 8 + e;
+                        const int dist = abs(apos - (n0 + key));
+                        sc[u][e] = __builtin_fmaf(sc[u][e], c2, al2 * (float)dist);
+                    }
+                cc = 1.f;
+            }
+
+            // ---- mask, running max (raw scores; cc > 0 so the scaled max is cc * max)
             const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
             float mx = kNegInf;
             if (need_mask) {
@@ -783,7 +807,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
                 mx = wave_max_xor(mx, 16);
                 mx = wave_max_xor(mx, 32);
             }
-            mx *= c2;
+            mx *= cc;
             const bool grow = mx > m_run + 8.f;
             if (__ballot(grow)) {
                 // rows that do not grow keep alpha = 1 (their m_run may still be -inf)
@@ -803,8 +827,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int e = 0; e < SPU; e += 2) {
-                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e], c2, nm));
-                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e + 1], c2, nm));
+                    const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e], cc, nm));
+                    const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[u][e + 1], cc, nm));
                     const unsigned int pp = E::pack2(p0, p1);
                     pk[u][e / 2] = pp;
                     // row sum of the bf16-rounded probabilities that feed the PV product
@@ -970,7 +994,8 @@ hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
     const int64_t units = plan.items_bound * (int64_t)p.Hk;
     const int64_t run = 8 * (int64_t)p.xcd_chunk;
     dim3 grid((unsigned)((units + run - 1) / run * run));
-    hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS>), grid, dim3(64 * WR), 0, s, p);
+    if (p.alibi) hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, true>), grid, dim3(64 * WR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, false>), grid, dim3(64 * WR), 0, s, p);
     return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ struct FwdParams {
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t* tok_nc;        // [total_q] chunks of each token's sequence (split only)
     int32_t f16;            // element type of q/k/v/out: 0 = bf16, 1 = fp16
+    const float* alibi;     // ALiBi slopes or nullptr: slope of (sequence b, head h) at alibi[b * alibi_sb + h]
+    int64_t alibi_sb;
     int32_t vec;            // 1 = 16-byte vector loads are legal for q/k/v/out
     int32_t fast_copy;      // 1 = interior K/V tiles may use uniform-base + lane-offset copies
     int32_t k_rowb, v_rowb; // bytes between consecutive key rows (paged: slot stride; packed: token stride)
