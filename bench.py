@@ -208,7 +208,7 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
 
 # ----------------------------------------------------------------- CPU leg
 
-def cpu_baseline(wl, work, decode: bool):
+def cpu_baseline(wl, work, decode: bool, alibi=None):
     """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
     import oracle
     oracle.build()
@@ -236,7 +236,7 @@ def cpu_baseline(wl, work, decode: bool):
             nseq += 1
         reps, t0 = 0, time.perf_counter()
         while True:  # repeat a small sample until the timing is at least ~3 s long
-            oracle.attention_workload(wl, token_sel=sel, nthreads=threads)
+            oracle.attention_workload(wl, token_sel=sel, nthreads=threads, alibi_slopes=alibi)
             reps += 1
             dt = time.perf_counter() - t0
             if dt >= 3.0:
@@ -256,7 +256,7 @@ def cpu_baseline(wl, work, decode: bool):
     sel[perm[:n]] = 1
     flops = 4.0 * D * H * float(rows_pairs[perm[:n]].sum())
     t0 = time.perf_counter()
-    oracle.attention_workload(wl, token_sel=sel, nthreads=threads)
+    oracle.attention_workload(wl, token_sel=sel, nthreads=threads, alibi_slopes=alibi)
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
             "kind": "oracle",
@@ -420,13 +420,15 @@ def bench_padded(args, fa, W, hip, dev, stream):
     ws_bytes = fa.fa_padded_workspace_bytes(*calls[0][:3])
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     sh = stream.cuda_stream
+    alibi_t = torch.from_numpy(W.alibi_slopes(H)).to(dev) if args.alibi else None
+    dal = fa._tdesc(alibi_t) if alibi_t is not None else None
 
     def step(i, ev_k=None):
         dq, dk, dv, do = calls[i % ncopies]
         if ev_k is not None:
             fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
         rc = fa.fa_padded_fwd(dq, dk, dv, do, scale, cfg["window_left"], cfg["window_right"], 0,
-                              workspace.data_ptr() if ws_bytes else 0, ws_bytes, sh)
+                              workspace.data_ptr() if ws_bytes else 0, ws_bytes, sh, dal)
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
@@ -468,7 +470,7 @@ def bench_padded(args, fa, W, hip, dev, stream):
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, work, decode)
+        cpu = cpu_baseline(wl, work, decode, W.alibi_slopes(wl.num_heads) if args.alibi else None)
     props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": "padded (batch-major) attention: prefill TFLOP/s (%MFMA peak); decode KV GB/s (%HBM)",
@@ -479,7 +481,7 @@ def bench_padded(args, fa, W, hip, dev, stream):
         "config": {"workload": "%s: %s" % (args.workload, cfg["desc"]), "batch": B, "seqlen_q": Sq,
                    "seqlen_k": Sk, "num_heads": H, "num_heads_k": Hk, "head_dim": D,
                    "window_left": cfg["window_left"], "window_right": cfg["window_right"],
-                   "parallelism": "single GPU"},
+                   "alibi": bool(args.alibi), "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "detail": {"main_kernel_ms_mean": round(kern_mean, 5), "event_sampled_steps": len(sampled),
@@ -503,6 +505,8 @@ def main(argv=None):
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of q/k/v/out (and the append's rows and pools)")
+    ap.add_argument("--alibi", action="store_true",
+                    help="forward and padded: add ALiBi (geometric slopes 2^(-8h/H), one per head)")
     ap.add_argument("--op", default="fwd", choices=["fwd", "append", "padded"],
                     help="fwd: the attention forward (default); append: the paged K/V append; "
                          "padded: the batch-major entry")
@@ -587,6 +591,8 @@ def main(argv=None):
         calls.append((dq, dk, dv, do, dbt, d))
     workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     sh = stream.cuda_stream
+    alibi_t = torch.from_numpy(W.alibi_slopes(wl.num_heads)).to(dev) if args.alibi else None
+    dal = fa._tdesc(alibi_t) if alibi_t is not None else None
 
     def step(i, ev_k=None):
         dq, dk, dv, do, dbt, d = calls[i % ncopies]
@@ -595,7 +601,7 @@ def main(argv=None):
         rc = fa.fa_varlen_fwd(dq, dk, dv, do, d["cu_q"].data_ptr(), d["cu_k"].data_ptr(), wl.batch,
                               dbt, wl.page_block_size, wl.softmax_scale, wl.window_left,
                               wl.window_right, 0, workspace.data_ptr() if ws_bytes else 0,
-                              ws_bytes, sh)
+                              ws_bytes, sh, dal)
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
@@ -650,7 +656,7 @@ def main(argv=None):
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, work, decode)
+        cpu = cpu_baseline(wl, work, decode, W.alibi_slopes(wl.num_heads) if args.alibi else None)
 
     props = torch.cuda.get_device_properties(dev)
     line = {
@@ -671,7 +677,7 @@ def main(argv=None):
             "batch": wl.batch, "total_q": int(wl.lens_q.sum()), "total_k": int(wl.lens_k.sum()),
             "num_heads": wl.num_heads, "num_heads_k": wl.num_heads_k, "head_dim": wl.head_dim,
             "page_block_size": wl.page_block_size, "window_left": wl.window_left,
-            "window_right": wl.window_right, "parallelism": "single GPU",
+            "window_right": wl.window_right, "alibi": bool(args.alibi), "parallelism": "single GPU",
         },
         "roofline": roof,
         "cpu_baseline": cpu,
