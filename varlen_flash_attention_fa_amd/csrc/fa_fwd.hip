@@ -146,7 +146,7 @@ __device__ __forceinline__ float wave_max_xor(float x, int mask) {
 }
 
 struct Item {
-    int b, rt, c, nc, gid;
+    int b, rt, c, nc, cl;  // cl: keys per chunk of this call
     int q0, Lq, k0, Lk;
 };
 
@@ -247,8 +247,16 @@ constexpr int kPlanThreads = 1024;
 constexpr int kCostBuckets = 128;
 constexpr int kLdsSeqs = 2048;  // sequences whose spans and item offsets stay in LDS
 
-__device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk) {
-    return p.max_chunks > 1 ? min(p.max_chunks, max(1, ceil_div(lk, p.chunk))) : 1;
+__device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk, int chunk) {
+    return p.max_chunks > 1 ? min(p.max_chunks, max(1, ceil_div(lk, chunk))) : 1;
+}
+
+// Candidate chunk sizes for a decode call whose planner may shrink the chunk:
+// 8/8 .. 4/8 of the base size, rounded up to whole key tiles.
+constexpr int kChunkCands = 5;
+__device__ __forceinline__ int chunk_cand(const FwdParams& p, int k) {
+    const int c = p.chunk * (8 - k) / 8;
+    return max(p.chunk_min, (c + p.chunk_align - 1) / p.chunk_align * p.chunk_align);
 }
 
 __device__ __forceinline__ int cost_bucket(int64_t cost) {
@@ -263,6 +271,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     __shared__ int4 s_span[kLdsSeqs];
     __shared__ int s_wsum[kPlanThreads / 64];
     __shared__ int s_hist[kCostBuckets];
+    __shared__ unsigned long long s_cand[kChunkCands];
+    __shared__ int s_chunk;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const bool cached = p.batch <= kLdsSeqs;
@@ -274,39 +284,88 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     if (split)  // split partials: chunks per token for the combine (0 = not in a sequence)
         for (int t = tid; t < p.total_q; t += kPlanThreads) p.tok_nc[t] = 0;
 
-    // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
-    // LDS step per 1024 sequences)
+    // Chunk size.  Work items of one call cost about the same, and the hardware
+    // runs `slots` of them at a time, so the kernel takes about
+    // ceil(items / slots) rounds of (chunk + per-item overhead).  When the base
+    // chunk needs more than one round, the candidate chunk with the smallest such
+    // estimate is taken and the items are counted again (fewer keys per item can
+    // fill the last round instead of leaving it nearly empty); within one round
+    // the kernel streams K/V at full bandwidth and smaller chunks would only add
+    // partials, so the base chunk stays.
+    int chunk = p.chunk;
     int carry = 0;
-    for (int base = 0; base < p.batch; base += kPlanThreads) {
-        const int b = base + tid;
-        int cnt = 0;
-        if (b < p.batch) {
-            const SeqSpan sp = seq_span(p, b);
-            if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
-            cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk);
-        }
-        int x = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) s_wsum[wave] = x;
-        __syncthreads();
-        if (wave == 0) {
-            int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
-#pragma unroll
-            for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
-                const int y = __shfl_up(w, o, 64);
-                if (lane >= o) w += y;
+    for (int attempt = 0; attempt < 2; ++attempt) {
+        // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
+        // LDS step per 1024 sequences)
+        carry = 0;
+        for (int base = 0; base < p.batch; base += kPlanThreads) {
+            const int b = base + tid;
+            int cnt = 0;
+            if (b < p.batch) {
+                const SeqSpan sp = seq_span(p, b);
+                if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
+                cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, chunk);
             }
-            if (lane < kPlanThreads / 64) s_wsum[lane] = w;
+            int x = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (lane == 63) s_wsum[wave] = x;
+            __syncthreads();
+            if (wave == 0) {
+                int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
+#pragma unroll
+                for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
+                    const int y = __shfl_up(w, o, 64);
+                    if (lane >= o) w += y;
+                }
+                if (lane < kPlanThreads / 64) s_wsum[lane] = w;
+            }
+            __syncthreads();
+            const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
+            if (b < p.batch) off[b] = carry + incl - cnt;
+            carry += s_wsum[kPlanThreads / 64 - 1];
+            __syncthreads();
+        }
+        if (attempt == 1 || !(split && p.chunk_adapt)) break;
+        if ((unsigned long long)carry * (unsigned long long)p.Hk <= (unsigned long long)max(1, p.slots)) break;
+        if (tid < kChunkCands) s_cand[tid] = 0;
+        if (tid == 0) s_chunk = chunk;
+        __syncthreads();
+        unsigned long long cnt[kChunkCands] = {};
+        for (int b = tid; b < p.batch; b += kPlanThreads) {
+            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+            const int tiles = ceil_div(sp.Lq * p.G, R);
+#pragma unroll
+            for (int k = 0; k < kChunkCands; ++k)
+                cnt[k] += (unsigned long long)tiles * seq_chunks(p, sp.Lk, chunk_cand(p, k));
+        }
+#pragma unroll
+        for (int k = 0; k < kChunkCands; ++k) {
+            unsigned long long x = cnt[k];
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+            if (lane == 0) atomicAdd(&s_cand[k], x);
         }
         __syncthreads();
-        const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
-        if (b < p.batch) off[b] = carry + incl - cnt;
-        carry += s_wsum[kPlanThreads / 64 - 1];
+        if (tid == 0) {
+            const unsigned long long slots = (unsigned long long)max(1, p.slots);
+            unsigned long long best = ~0ull;
+            for (int k = 0; k < kChunkCands; ++k) {
+                const int c = chunk_cand(p, k);
+                const unsigned long long units = s_cand[k] * (unsigned long long)p.Hk;
+                const unsigned long long est = (units + slots - 1) / slots * (unsigned long long)(c + 2 * R + 64);
+                if (est < best) {
+                    best = est;
+                    s_chunk = c;
+                }
+            }
+        }
         __syncthreads();
+        if (s_chunk == chunk) break;
+        chunk = s_chunk;
     }
     const int total = min(carry, p.items_bound);
     if (tid == 0) {
@@ -317,7 +376,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     if (split)
         for (int b = tid; b < p.batch; b += kPlanThreads) {
             const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-            const int nc = seq_chunks(p, sp.Lk);
+            const int nc = seq_chunks(p, sp.Lk, chunk);
             for (int t = sp.q0; t < sp.q0 + sp.Lq; ++t) p.tok_nc[t] = nc;
         }
 
@@ -333,7 +392,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
             const int b = lo;
             const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
             const int lq = sp.Lq, lk = sp.Lk;
-            const int nc = seq_chunks(p, lk);
+            const int nc = seq_chunks(p, lk, chunk);
             const int local = i - off[b];
             const int rt = local / nc, c = local % nc;
             const int nrows = lq * p.G;
@@ -342,8 +401,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
             const Range z = row_range(p, r1 / p.G, lq, lk);
             int kb = a.lo, ke = z.hi;
             if (split) {
-                kb = max(kb, c * p.chunk);
-                ke = min(ke, (c + 1) * p.chunk);
+                kb = max(kb, c * chunk);
+                ke = min(ke, (c + 1) * chunk);
             }
             const int64_t cost = (int64_t)max(0, ke - kb) * (r1 - r0 + 1) + (r1 - r0 + 1);
             const int bucket = cost_bucket(cost);
@@ -351,7 +410,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 atomicAdd(&s_hist[bucket], 1);
             } else {
                 const int pos = atomicAdd(&s_hist[bucket], 1);
-                p.items[2 * pos] = make_int4(b, rt, c | (nc << 16), 0);
+                p.items[2 * pos] = make_int4(b, rt, c | (nc << 16), chunk);
                 p.items[2 * pos + 1] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             }
         }
@@ -429,7 +488,7 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
         it.rt = d.y;
         it.c = d.z & 0xffff;
         it.nc = d.z >> 16;
-        it.gid = d.w;
+        it.cl = d.w;
         it.q0 = e.x;
         it.Lq = e.y;
         it.k0 = e.z;
@@ -448,8 +507,8 @@ __global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_
     const Range rl = row_range(p, r_last / p.G, Lq, Lk);
     int kb = rf.lo, ke = rl.hi;
     if (split) {
-        kb = max(kb, it.c * p.chunk);
-        ke = min(ke, (it.c + 1) * p.chunk);
+        kb = max(kb, it.c * it.cl);
+        ke = min(ke, (it.c + 1) * it.cl);
     }
 
     // this lane's row
@@ -988,8 +1047,33 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
 
 hipError_t g_last = hipSuccess;
 
+// With `slots` set, report how many workgroups of the kernel the launch would
+// use can be resident on the whole GPU at once instead of launching it.
 template <class E, int DP, int MR, int WR, int BN, int NS>
-hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s) {
+hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s, int* slots = nullptr) {
+    if (slots) {
+        static int per_cu = -1;  // per kernel instantiation; the same on every CU of this target
+        if (per_cu < 0) {
+            int nb = 0;
+            const void* fn = p.alibi ? reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, true>)
+                                     : reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, false>);
+            hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * WR, 0);
+            if (e != hipSuccess) return e;
+            per_cu = nb;
+        }
+        int dev = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        static int cus_of[64] = {};  // compute units per device id
+        int cus = (dev >= 0 && dev < 64) ? cus_of[dev] : 0;
+        if (cus <= 0) {
+            e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+            if (e != hipSuccess) return e;
+            if (dev >= 0 && dev < 64) cus_of[dev] = cus;
+        }
+        *slots = std::max(1, per_cu * cus);
+        return hipSuccess;
+    }
     // one workgroup per (item, K/V head) unit, padded to whole runs on all 8 XCDs
     const int64_t units = plan.items_bound * (int64_t)p.Hk;
     const int64_t run = 8 * (int64_t)p.xcd_chunk;
@@ -1007,28 +1091,28 @@ hipError_t launch_combine(const FwdParams& p, hipStream_t s) {
 }
 
 template <class E, int DP>
-hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s) {
+hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s, int* slots) {
     // one LDS stage here too: it frees registers and LDS for 3 resident workgroups
     // per CU, which beat a prefetching second stage (+6-8% on long prefill)
     if (plan.kind == KIND_PREFILL) {
-        if constexpr (DP <= 128) return launch_attn<E, DP, 32, 4, 64, 1>(plan, p, s);
-        else if constexpr (DP == 256) return launch_attn<E, DP, 32, 4, 32, 2>(plan, p, s);
-        else return launch_attn<E, DP, 16, 4, 32, 2>(plan, p, s);
+        if constexpr (DP <= 128) return launch_attn<E, DP, 32, 4, 64, 1>(plan, p, s, slots);
+        else if constexpr (DP == 256) return launch_attn<E, DP, 32, 4, 32, 2>(plan, p, s, slots);
+        else return launch_attn<E, DP, 16, 4, 32, 2>(plan, p, s, slots);
     }
     // decode: 16 rows per wave, keys split over work items, one LDS stage: HBM
     // latency is hidden by the number of resident workgroups (LDS-limited),
     // which beats deeper per-wave pipelines on this path
-    if (plan.wr == 1) return launch_attn<E, DP, 16, 1, 32, 1>(plan, p, s);
-    return launch_attn<E, DP, 16, 4, 32, 1>(plan, p, s);
+    if (plan.wr == 1) return launch_attn<E, DP, 16, 1, 32, 1>(plan, p, s, slots);
+    return launch_attn<E, DP, 16, 4, 32, 1>(plan, p, s, slots);
 }
 
 template <class E>
-hipError_t launch_main(const Plan& plan, const FwdParams& p, hipStream_t s) {
+hipError_t launch_main(const Plan& plan, const FwdParams& p, hipStream_t s, int* slots = nullptr) {
     switch (plan.dp) {
-        case 64: return launch_dp<E, 64>(plan, p, s);
-        case 128: return launch_dp<E, 128>(plan, p, s);
-        case 256: return launch_dp<E, 256>(plan, p, s);
-        default: return launch_dp<E, 512>(plan, p, s);
+        case 64: return launch_dp<E, 64>(plan, p, s, slots);
+        case 128: return launch_dp<E, 128>(plan, p, s, slots);
+        case 256: return launch_dp<E, 256>(plan, p, s, slots);
+        default: return launch_dp<E, 512>(plan, p, s, slots);
     }
 }
 
@@ -1071,6 +1155,8 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.wr = 4;
         P.bn = P.dp <= 128 ? 64 : 32;
         P.chunk = INT_MAX;
+        P.chunk_min = INT_MAX;
+        P.adapt = false;
         P.max_chunks = 1;
         // Few row tiles over long key ranges (chunked prefill on a long cache) give
         // too few, too uneven work items for the chip: cut the keys into halves of
@@ -1088,6 +1174,7 @@ int make_plan(const Shapes& s, Plan* plan) {
             if (mc > 4096) return FA_ERR_ARGUMENT;
             if (mc > 1) {
                 P.chunk = (int)chunk;
+                P.chunk_min = (int)chunk;
                 P.max_chunks = (int)mc;
             }
         }
@@ -1095,15 +1182,21 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.mr = 16;
         P.wr = rows_avg <= 16 ? 1 : 4;
         P.bn = 32;
-        int chunk = P.dp <= 128 ? 512 : 1024;
-        chunk = env_int("FA_SPLIT_KEYS", chunk);
+        // base chunk; the planner may shrink it to half (a forced size is kept)
+        const int forced = env_int("FA_SPLIT_KEYS", 0);
+        int chunk = forced > 0 ? forced : (P.dp <= 128 ? 512 : 1024);
         if (chunk < P.bn) chunk = P.bn;
         chunk = (chunk + P.bn - 1) / P.bn * P.bn;
         P.chunk = chunk;
-        const int64_t mc = std::max<int64_t>(1, (s.max_lk + chunk - 1) / chunk);
+        P.adapt = forced <= 0;
+        P.chunk_min = P.adapt ? std::max(P.bn, (chunk / 2 + P.bn - 1) / P.bn * P.bn) : chunk;
+        const int64_t mc = std::max<int64_t>(1, (s.max_lk + P.chunk_min - 1) / P.chunk_min);
         if (mc > 4096) return FA_ERR_ARGUMENT;
         P.max_chunks = (int)mc;
-        if (P.max_chunks == 1) P.chunk = INT_MAX;
+        if (P.max_chunks == 1) {
+            P.chunk = P.chunk_min = INT_MAX;
+            P.adapt = false;
+        }
     }
     P.rows = P.mr * P.wr;
     const int64_t tiles = (s.total_q * G + P.rows - 1) / P.rows + s.batch;
@@ -1140,9 +1233,20 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     p.rows = plan.rows;
     p.items_bound = (int32_t)plan.items_bound;
     p.xcd_chunk = plan.xcd_chunk;
+    p.chunk = plan.chunk;
+    p.chunk_min = plan.chunk_min;
+    p.chunk_align = plan.bn;
+    p.chunk_adapt = plan.adapt ? 1 : 0;
     hipError_t e = hipSuccess;
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
-    e = hipGetLastError();
+    if (plan.adapt) {
+        int slots = 0;
+        e = p.f16 ? launch_main<EF16>(plan, p, s, &slots) : launch_main<EBf16>(plan, p, s, &slots);
+        p.slots = slots;
+    }
+    if (e == hipSuccess) {
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
+        e = hipGetLastError();
+    }
     if (e == hipSuccess && ev_start) e = hipEventRecord(static_cast<hipEvent_t>(ev_start), s);
     if (e == hipSuccess) e = p.f16 ? launch_main<EF16>(plan, p, s) : launch_main<EBf16>(plan, p, s);
     if (e == hipSuccess && ev_stop) e = hipEventRecord(static_cast<hipEvent_t>(ev_stop), s);

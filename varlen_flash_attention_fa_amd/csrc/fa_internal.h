@@ -29,7 +29,11 @@ struct FwdParams {
     int32_t max_lk;         // paged: block_table width * page; non-paged: total_k
     int32_t num_blocks;     // paged pool size (block ids are clamped into it)
     int32_t window_left, window_right;
-    int32_t chunk;          // keys per split (split only if max_chunks > 1)
+    int32_t chunk;          // keys per split (split only if max_chunks > 1); the planner may shrink it
+    int32_t chunk_min;      // smallest chunk the workspace allows (decode: chunk / 2)
+    int32_t chunk_align;    // chunk sizes are multiples of this (the key tile)
+    int32_t chunk_adapt;    // 1 = the planner picks the chunk from the sequence lengths
+    int32_t slots;          // workgroups of the main kernel resident at once (whole GPU)
     int32_t max_chunks;
     int32_t rows;           // rows per work item (MFMA rows per wave * waves)
     int32_t items_bound;    // upper bound of the number of work items per K/V head
@@ -65,7 +69,9 @@ struct Plan {
     int wr;         // waves per workgroup (each owns mr rows)
     int bn;         // keys per LDS tile
     int rows;       // rows per workgroup = mr * wr
-    int chunk;      // keys per split
+    int chunk;      // keys per split (base size)
+    int chunk_min;  // smallest chunk the planner may pick (workspace is sized for it)
+    bool adapt;     // planner picks the chunk
     int max_chunks; // upper bound of splits per sequence
     int64_t items_bound;  // upper bound of work items per K/V head
     int xcd_chunk;        // work units per run on one XCD
