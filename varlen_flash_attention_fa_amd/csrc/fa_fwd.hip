@@ -436,7 +436,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
 template <class E, int DP, int MR, int WR, int BN, int NS, bool AL>
-__global__ __launch_bounds__(64 * WR, (WR == 4 && DP <= 128 ? 2 : 1)) void attn_fwd_kernel(const FwdParams p) {
+// At least two waves per SIMD for the 4-wave D<=128 kernels and the 4-wave
+// D256/D512 decode kernels (the D512 one would otherwise take 380 registers and
+// keep one wave per SIMD where its 64 KiB of LDS allow two workgroups per CU:
+// spec-decode D512 MQA +30%).
+__global__ __launch_bounds__(64 * WR) __attribute__((amdgpu_waves_per_eu(
+    (WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256) ? 2 : 1, 8))) void
+attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR, E> M;
     typedef typename M::acc_t acc_t;
     constexpr int NT = 64 * WR;
