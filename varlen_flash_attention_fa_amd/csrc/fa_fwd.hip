@@ -183,10 +183,30 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const unsigned char* ptr) {
     return __builtin_bit_cast(u32x2, r);
 }
 
+// LDS byte address of a pointer into shared memory.
+__device__ __forceinline__ unsigned lds_u32(const unsigned char* p) {
+    return (unsigned)(size_t)(const __attribute__((address_space(3))) unsigned char*)p;
+}
+
 // One 16-byte global -> LDS copy per lane (global_load_lds_dwordx4): lane l's
-// data lands at lds_base + 16*l.  lds_base must be wave-uniform.
-__device__ __forceinline__ void copy16_to_lds(const uint16_t* gsrc, unsigned char* lds_base) {
-    __builtin_amdgcn_global_load_lds((const void*)gsrc, (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// data lands at LDS byte address lds + 16*l; lds (in M0) must be wave-uniform.
+// Written as inline assembly so the compiler does not treat the copy as an LDS
+// store: it would otherwise wait for every copy in flight before any later LDS
+// read, which serialises loading the next tile with computing on this one.
+// Completion is tracked by the kernel itself (vmcnt waits + barriers).  The
+// instruction between the M0 write and the copy is the one wait state the copy
+// needs after M0 is written.
+__device__ __forceinline__ void copy16_to_lds(const uint16_t* gsrc, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :: "v"(gsrc), "s"(lds) : "m0");
+}
+// Same, with a wave-uniform 64-bit base and a per-lane 32-bit byte offset.  The
+// base is first copied by a scalar move, so the copy never reads an SGPR that a
+// vector instruction has just written.
+__device__ __forceinline__ void copy16_to_lds_sv(const unsigned char* sbase, unsigned voff, unsigned lds) {
+    unsigned long long tmp;
+    asm volatile("s_mov_b32 m0, %2\n\ts_mov_b64 %0, %3\n\tglobal_load_lds_dwordx4 %1, %0"
+                 : "=&s"(tmp) : "v"(voff), "s"(lds), "s"(sbase) : "m0");
 }
 
 constexpr int kPageCap = 256;
@@ -436,12 +456,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
 template <class E, int DP, int MR, int WR, int BN, int NS, bool AL>
-// At least two waves per SIMD for the 4-wave D<=128 kernels and the 4-wave
-// D256/D512 decode kernels (the D512 one would otherwise take 380 registers and
-// keep one wave per SIMD where its 64 KiB of LDS allow two workgroups per CU:
-// spec-decode D512 MQA +30%).
+// Waves per SIMD asked of the compiler: three for the D<=128 prefill kernel
+// without ALiBi (its 33 KiB of LDS allow three workgroups per CU; the staggered
+// K/V copies would otherwise raise it to 193 registers and two waves; at 168 a
+// few values that live across the tile loop spill, outside the loop); two for
+// the other 4-wave D<=128 kernels and the 4-wave D256/D512 decode kernels (the
+// D512 one would otherwise take 380 registers and keep one wave per SIMD where
+// its 64 KiB of LDS allow two workgroups per CU).
 __global__ __launch_bounds__(64 * WR) __attribute__((amdgpu_waves_per_eu(
-    (WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256) ? 2 : 1, 8))) void
+    (WR == 4 && DP <= 128 && MR == 32 && !AL) ? 3 : ((WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256)) ? 2 : 1, 8))) void
 attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR, E> M;
     typedef typename M::acc_t acc_t;
@@ -463,6 +486,7 @@ attn_fwd_kernel(const FwdParams p) {
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * 2 * TILEB];
     __shared__ int s_pages[kPageCap];
+    const unsigned smem_lds = lds_u32(smem);
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -594,62 +618,81 @@ attn_fwd_kernel(const FwdParams p) {
         }
         const int ntiles = (seg1 - seg0 + BN - 1) / BN;
 
-        // issue the copies of tile t of this segment into stage t % NS
-        auto issue = [&](int t) {
+        // page index and slot of the first key of the next tile whose K (index 0)
+        // or V (index 1) copies are issued (paged); each tensor's tiles are issued
+        // in increasing order, so both advance by BN per issued tile
+        int nx_page[2] = {pg_first, pg_first}, nx_slot[2] = {0, 0};
+        const int pg_last = paged ? (seg1 - 1) / P : 0;
+        if (paged) nx_slot[0] = nx_slot[1] = seg0 - pg_first * P;
+
+        // issue the copies of tile t of this segment into stage t % NS: which = 0
+        // K only, 1 V only, 2 both
+        auto issue = [&](int t, int which) {
             const int ts = seg0 + t * BN;
             unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
             unsigned char* vbuf = kbuf + TILEB;
-            int pg0 = 0, pg1 = 0, base0 = 0;
-            if (paged) {
-                const int p0 = ts / P;
-                const int p1 = min(p0 + 1, (seg1 - 1) / P);  // only pages staged for this segment
-                pg0 = __builtin_amdgcn_readfirstlane(s_pages[p0 - pg_first]);
-                pg1 = __builtin_amdgcn_readfirstlane(s_pages[p1 - pg_first]);
-                base0 = p0 * P;
+            const int sx = which == 1 ? 1 : 0;
+            const int t_page = nx_page[sx], t_slot = nx_slot[sx];
+            if (paged) {  // P >= 32 and BN <= 64: at most two page steps
+#pragma unroll
+                for (int x = 0; x < 2; ++x) {
+                    if (x == sx || which == 2) {
+                        nx_slot[x] += BN;
+                        if (nx_slot[x] >= P) { nx_slot[x] -= P; ++nx_page[x]; }
+                        if (nx_slot[x] >= P) { nx_slot[x] -= P; ++nx_page[x]; }
+                    }
+                }
             }
             const int ln = opaque_lane();
             const int lrow = ln / CH;
             const int lpos = ln % CH;
-            // Fast path for interior tiles: the RPI rows of one copy instruction lie in
-            // one page, so the address is a wave-uniform base (page, first row, head)
-            // plus a per-lane offset (row within the copy, swizzled chunk) that does
-            // not depend on the tile.  The swizzle splits as (lane part) ^ (uniform
-            // part) because the copy's first row is a multiple of RPI.
+            // Fast path for interior tiles: the W rows one wave copies lie in one page
+            // (W divides 32, which divides P, and tiles start at multiples of BN), so
+            // every copy address is a wave-uniform base (page, first row, head) plus a
+            // per-lane offset (row within the copy, swizzled chunk).  The swizzle
+            // splits as (lane part) ^ (uniform part) because each copy's first row is
+            // a multiple of RPI.
             if (p.fast_copy && ts >= kb && ts + BN <= ke) {
+                constexpr int W = NI * RPI;
+                static_assert(32 % W == 0, "a wave's copy rows must stay inside one page");
+                const int wv = __builtin_amdgcn_readfirstlane(wave);  // lets the compiler keep bases scalar
+                const unsigned char *kw, *vw;
+                if (paged) {
+                    int ws = t_slot + wv * W, wp = t_page;
+                    if (ws >= P) { ws -= P; ++wp; }
+                    if (ws >= P) { ws -= P; ++wp; }
+                    const int pg = __builtin_amdgcn_readfirstlane(s_pages[wp - pg_first]);
+                    kw = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg * p.k_s0 + (int64_t)ws * p.k_s1 + (int64_t)hk * p.k_s2);
+                    vw = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg * p.v_s0 + (int64_t)ws * p.v_s1 + (int64_t)hk * p.v_s2);
+                } else {
+                    const int64_t row = it.k0 + ts + wv * W;
+                    kw = reinterpret_cast<const unsigned char*>(p.k + row * p.k_s0 + kbx + (int64_t)hk * p.k_s1);
+                    vw = reinterpret_cast<const unsigned char*>(p.v + row * p.v_s0 + vbx + (int64_t)hk * p.v_s1);
+                }
                 const int xk = lpos ^ (lrow & SWK);
                 const int xv = lpos ^ ((2 * lrow) & SWV);
                 const unsigned lk_off = (unsigned)lrow * (unsigned)p.k_rowb;
                 const unsigned lv_off = (unsigned)lrow * (unsigned)p.v_rowb;
-                // per tile: byte pointers to row 0 of the tile's page(s) (paged) or to
-                // the tile's first row (packed); per copy: a 32-bit row offset
-                const unsigned char *kp0, *kp1, *vp0, *vp1;
-                int slot0 = 0;
-                if (paged) {
-                    kp0 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg0 * p.k_s0 + (int64_t)hk * p.k_s2);
-                    vp0 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg0 * p.v_s0 + (int64_t)hk * p.v_s2);
-                    kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg1 * p.k_s0 + (int64_t)hk * p.k_s2);
-                    vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg1 * p.v_s0 + (int64_t)hk * p.v_s2);
-                    slot0 = ts - base0;
-                } else {
-                    kp0 = kp1 = reinterpret_cast<const unsigned char*>(p.k + (int64_t)(it.k0 + ts) * p.k_s0 + kbx + (int64_t)hk * p.k_s1);
-                    vp0 = vp1 = reinterpret_cast<const unsigned char*>(p.v + (int64_t)(it.k0 + ts) * p.v_s0 + vbx + (int64_t)hk * p.v_s1);
-                }
-                const int wv = __builtin_amdgcn_readfirstlane(wave);  // lets the compiler keep bases scalar
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    const int r0 = (wv * NI + i) * RPI;  // first row of this copy (uniform)
-                    int sl = slot0 + r0;
-                    const bool second = paged && sl >= P;
-                    sl = second ? sl - P : sl;
-                    const unsigned char* kb_ = (second ? kp1 : kp0) + (unsigned)sl * (unsigned)p.k_rowb;
-                    const unsigned char* vb_ = (second ? vp1 : vp0) + (unsigned)sl * (unsigned)p.v_rowb;
+                    const int r0 = wv * W + i * RPI;  // tile row of the copy's first lane row (uniform)
                     const unsigned vk = lk_off + ((unsigned)(xk ^ (r0 & SWK)) << 4);
                     const unsigned vv = lv_off + ((unsigned)(xv ^ ((2 * r0) & SWV)) << 4);
-                    unsigned char* dst = smem + (t % NS) * 2 * TILEB + (wv * NI + i) * 1024;
-                    copy16_to_lds(reinterpret_cast<const uint16_t*>(kb_ + vk), dst);
-                    copy16_to_lds(reinterpret_cast<const uint16_t*>(vb_ + vv), dst + TILEB);
+                    const unsigned dst = smem_lds + (unsigned)((t % NS) * 2 * TILEB + (wv * NI + i) * 1024);
+                    if (which != 1) copy16_to_lds_sv(kw + (size_t)(i * RPI) * p.k_rowb, vk, dst);
+                    if (which != 0) copy16_to_lds_sv(vw + (size_t)(i * RPI) * p.v_rowb, vv, dst + TILEB);
                 }
-            } else if (vec) {
+                return;
+            }
+            // boundary tiles: per-lane rows clamped into [kb, ke); a tile spans at
+            // most two pages
+            int pg0 = 0, pg1 = 0, base0 = 0;
+            if (paged) {
+                pg0 = __builtin_amdgcn_readfirstlane(s_pages[t_page - pg_first]);
+                pg1 = __builtin_amdgcn_readfirstlane(s_pages[min(t_page + 1, pg_last) - pg_first]);
+                base0 = ts - t_slot;
+            }
+            if (vec) {
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int rr = (wave * NI + i) * RPI + lrow;
@@ -669,9 +712,9 @@ attn_fwd_kernel(const FwdParams p) {
                     int cv = lpos ^ ((2 * rr) & SWV);
                     ck = ck < nchv ? ck : 0;
                     cv = cv < nchv ? cv : 0;
-                    unsigned char* dst = smem + (t % NS) * 2 * TILEB + (wave * NI + i) * 1024;
-                    copy16_to_lds(p.k + offk + ck * 8, dst);
-                    copy16_to_lds(p.v + offv + cv * 8, dst + TILEB);
+                    const unsigned dst = smem_lds + (unsigned)__builtin_amdgcn_readfirstlane((t % NS) * 2 * TILEB + (wave * NI + i) * 1024);
+                    if (which != 1) copy16_to_lds(p.k + offk + ck * 8, dst);
+                    if (which != 0) copy16_to_lds(p.v + offv + cv * 8, dst + TILEB);
                 }
             } else {
                 // unaligned or odd head dim: element-wise loads, zero fill, plain LDS stores
@@ -695,30 +738,43 @@ attn_fwd_kernel(const FwdParams p) {
                     const int ck = lpos ^ (rr & SWK);
                     const int cv = lpos ^ ((2 * rr) & SWV);
                     const u32x4 zk = u32x4{0u, 0u, 0u, 0u};
-                    const u32x4 valk = ok ? load8(rowk, ck * 8, D, false) : zk;
-                    const u32x4 valv = ok ? load8(rowv, cv * 8, D, false) : zk;
-                    *reinterpret_cast<u32x4*>(kbuf + rr * ROWB + lpos * 16) = valk;
-                    *reinterpret_cast<u32x4*>(vbuf + rr * ROWB + lpos * 16) = valv;
+                    if (which != 1) {
+                        const u32x4 valk = ok ? load8(rowk, ck * 8, D, false) : zk;
+                        *reinterpret_cast<u32x4*>(kbuf + rr * ROWB + lpos * 16) = valk;
+                    }
+                    if (which != 0) {
+                        const u32x4 valv = ok ? load8(rowv, cv * 8, D, false) : zk;
+                        *reinterpret_cast<u32x4*>(vbuf + rr * ROWB + lpos * 16) = valv;
+                    }
                 }
             }
         };
 
+        // One stage (NS = 1), staggered: V(t) is copied while S(t) and the softmax
+        // of tile t run, K(t+1) while the softmax and PV of tile t run; each
+        // buffer is refilled once every wave is past its last read of it.
+        // NS >= 2: whole tiles NS-1 ahead.
+        if constexpr (NS == 1) {
+            if (ntiles > 0) {
+                __syncthreads();  // every wave is done with the previous segment's K tile
+                issue(0, 0);
+            }
+        } else {
 #pragma unroll
-        for (int t = 0; t < NS - 1; ++t)
-            if (t < ntiles) issue(t);
+            for (int t = 0; t < NS - 1; ++t)
+                if (t < ntiles) issue(t, 2);
+        }
 
         for (int t = 0; t < ntiles; ++t) {
             if constexpr (NS == 1) {
-                // single stage: copy, wait, compute (latency is hidden by other waves)
-                __syncthreads();  // every wave is done with the previous tile
-                issue(t);
-                wait_vmcnt<0>();
-                __syncthreads();
+                wait_vmcnt<0>();  // K(t) has landed (no other copy is in flight)
+                __syncthreads();  // K(t) visible to every wave; every wave is done with V(t-1)
+                issue(t, 1);
             } else {
                 if (t + NS - 2 < ntiles) wait_vmcnt<(NS >= 2 ? (NS - 2) * 2 * NI : 0)>();
                 else wait_vmcnt<0>();
                 __syncthreads();  // tile t is in LDS for every wave; stage (t-1)%NS is free
-                if (t + NS - 1 < ntiles) issue(t + NS - 1);
+                if (t + NS - 1 < ntiles) issue(t + NS - 1, 2);
             }
 
             const int n0 = seg0 + t * BN;
@@ -830,6 +886,11 @@ attn_fwd_kernel(const FwdParams p) {
                 }
             }
 
+            if constexpr (NS == 1) {
+                __syncthreads();  // every wave is done with K(t)
+                if (t + 1 < ntiles) issue(t + 1, 0);
+            }
+
             // ---- ALiBi (when slopes are given): scores become c2 * s + al2 * |apos - n|,
             // already scaled, so the rest of the tile uses the factor cc = 1
             float cc = c2;
@@ -908,6 +969,13 @@ attn_fwd_kernel(const FwdParams p) {
                 rs += __shfl_xor(rs, 32, 64);
             }
             l_run += rs;
+
+            if constexpr (NS == 1) {
+                // V(t) has landed: only K(t+1)'s NI copies per lane may still be in flight
+                if (t + 1 < ntiles) wait_vmcnt<NI>();
+                else wait_vmcnt<0>();
+                __syncthreads();  // V(t) visible to every wave
+            }
 
             // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  Per tile, the
             // lane's two read addresses (rows r0, r0 + 4) are built for the first 16
