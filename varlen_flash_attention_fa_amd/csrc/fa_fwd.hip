@@ -271,11 +271,12 @@ __device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk, int chunk)
     return p.max_chunks > 1 ? min(p.max_chunks, max(1, ceil_div(lk, chunk))) : 1;
 }
 
-// Candidate chunk sizes for a decode call whose planner may shrink the chunk:
-// 8/8 .. 4/8 of the base size, rounded up to whole key tiles.
-constexpr int kChunkCands = 5;
+// Candidate chunk sizes for a decode call whose planner may resize the chunk:
+// 1/2 .. 2 times the base size, rounded up to whole key tiles.
+constexpr int kChunkCands = 9;
 __device__ __forceinline__ int chunk_cand(const FwdParams& p, int k) {
-    const int c = p.chunk * (8 - k) / 8;
+    constexpr int eighths[kChunkCands] = {4, 5, 6, 7, 8, 10, 12, 14, 16};
+    const int c = (int)((int64_t)p.chunk * eighths[k] / 8);
     return max(p.chunk_min, (c + p.chunk_align - 1) / p.chunk_align * p.chunk_align);
 }
 
@@ -307,11 +308,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     // Chunk size.  Work items of one call cost about the same, and the hardware
     // runs `slots` of them at a time, so the kernel takes about
     // ceil(items / slots) rounds of (chunk + per-item overhead).  When the base
-    // chunk needs more than one round, the candidate chunk with the smallest such
-    // estimate is taken and the items are counted again (fewer keys per item can
-    // fill the last round instead of leaving it nearly empty); within one round
-    // the kernel streams K/V at full bandwidth and smaller chunks would only add
-    // partials, so the base chunk stays.
+    // chunk needs more than one round, or fills less than half of one, the
+    // candidate chunk with the smallest such estimate is taken and the items are
+    // counted again: fewer keys per item can fill the last round instead of
+    // leaving it nearly empty, more keys per item can save a round, and an
+    // underfilled round gains parallelism from smaller items.  A round that is at
+    // least half full already streams K/V at full bandwidth, and smaller chunks
+    // would only add partials, so the base chunk stays.
     int chunk = p.chunk;
     int carry = 0;
     for (int attempt = 0; attempt < 2; ++attempt) {
@@ -350,7 +353,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
             __syncthreads();
         }
         if (attempt == 1 || !(split && p.chunk_adapt)) break;
-        if ((unsigned long long)carry * (unsigned long long)p.Hk <= (unsigned long long)max(1, p.slots)) break;
+        {
+            const unsigned long long units = (unsigned long long)carry * (unsigned long long)p.Hk;
+            const unsigned long long slots = (unsigned long long)max(1, p.slots);
+            if (units <= slots && 2 * units >= slots) break;
+        }
         if (tid < kChunkCands) s_cand[tid] = 0;
         if (tid == 0) s_chunk = chunk;
         __syncthreads();
@@ -1256,9 +1263,10 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.mr = 16;
         P.wr = rows_avg <= 16 ? 1 : 4;
         P.bn = 32;
-        // base chunk; the planner may shrink it to half (a forced size is kept)
+        // base chunk; the planner may resize it from half to twice (a forced size
+        // is kept)
         const int forced = env_int("FA_SPLIT_KEYS", 0);
-        int chunk = forced > 0 ? forced : (P.dp <= 128 ? 512 : 1024);
+        int chunk = forced > 0 ? forced : 1024;
         if (chunk < P.bn) chunk = P.bn;
         chunk = (chunk + P.bn - 1) / P.bn * P.bn;
         P.chunk = chunk;
