@@ -141,9 +141,21 @@ __device__ __forceinline__ u32x4 load8(const uint16_t* base, int d0, int D, bool
 }
 
 
-__device__ __forceinline__ float wave_max_xor(float x, int mask) {
-    return fmaxf(x, __shfl_xor(x, mask, 64));
+// Values of lanes l and l^32 (permlane32 swap) or l and l^16 (permlane16 swap),
+// as a pair that is the same on both lanes: one VALU instruction instead of an
+// LDS permute.
+__device__ __forceinline__ float2 pair_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
 }
+__device__ __forceinline__ float2 pair_xor16(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return float2{__uint_as_float(r[0]), __uint_as_float(r[1])};
+}
+__device__ __forceinline__ float max_xor32(float x) { const float2 r = pair_xor32(x); return fmaxf(r.x, r.y); }
+__device__ __forceinline__ float max_xor16(float x) { const float2 r = pair_xor16(x); return fmaxf(r.x, r.y); }
+__device__ __forceinline__ float sum_xor32(float x) { const float2 r = pair_xor32(x); return r.x + r.y; }
+__device__ __forceinline__ float sum_xor16(float x) { const float2 r = pair_xor16(x); return r.x + r.y; }
 
 struct Item {
     int b, rt, c, nc, cl;  // cl: keys per chunk of this call
@@ -935,10 +947,9 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int e = 0; e < SPU; ++e) mx = fmaxf(mx, sc[u][e]);
             if constexpr (MR == 32) {
-                mx = wave_max_xor(mx, 32);
+                mx = max_xor32(mx);
             } else {
-                mx = wave_max_xor(mx, 16);
-                mx = wave_max_xor(mx, 32);
+                mx = max_xor32(max_xor16(mx));
             }
             mx *= cc;
             const bool grow = mx > m_run + 8.f;
@@ -970,10 +981,9 @@ attn_fwd_kernel(const FwdParams p) {
                 }
             float rs = rs0 + rs1;
             if constexpr (MR == 32) {
-                rs += __shfl_xor(rs, 32, 64);
+                rs = sum_xor32(rs);
             } else {
-                rs += __shfl_xor(rs, 16, 64);
-                rs += __shfl_xor(rs, 32, 64);
+                rs = sum_xor32(sum_xor16(rs));
             }
             l_run += rs;
 
