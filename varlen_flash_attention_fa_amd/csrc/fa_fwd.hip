@@ -286,9 +286,10 @@ __device__ __forceinline__ int seq_chunks(const FwdParams& p, int lk, int chunk)
 // Candidate chunk sizes for a decode call whose planner may resize the chunk:
 // 1/2 .. 2 times the base size, rounded up to whole key tiles.
 constexpr int kChunkCands = 9;
+constexpr int kBaseCand = 4;  // the candidate equal to the base size
 __device__ __forceinline__ int chunk_cand(const FwdParams& p, int k) {
-    constexpr int eighths[kChunkCands] = {4, 5, 6, 7, 8, 10, 12, 14, 16};
-    const int c = (int)((int64_t)p.chunk * eighths[k] / 8);
+    const int eighths = k <= 4 ? 4 + k : 2 * k;  // 4, 5, 6, 7, 8, 10, 12, 14, 16
+    const int c = (int)((int64_t)p.chunk * eighths / 8);
     return max(p.chunk_min, (c + p.chunk_align - 1) / p.chunk_align * p.chunk_align);
 }
 
@@ -314,8 +315,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     const int R = p.rows;
 
     for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_hist[i] = 0;
-    if (split)  // split partials: chunks per token for the combine (0 = not in a sequence)
-        for (int t = tid; t < p.total_q; t += kPlanThreads) p.tok_nc[t] = 0;
 
     // Chunk size.  Work items of one call cost about the same, and the hardware
     // runs `slots` of them at a time, so the kernel takes about
@@ -328,54 +327,15 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     // least half full already streams K/V at full bandwidth, and smaller chunks
     // would only add partials, so the base chunk stays.
     int chunk = p.chunk;
-    int carry = 0;
-    for (int attempt = 0; attempt < 2; ++attempt) {
-        // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
-        // LDS step per 1024 sequences)
-        carry = 0;
-        for (int base = 0; base < p.batch; base += kPlanThreads) {
-            const int b = base + tid;
-            int cnt = 0;
-            if (b < p.batch) {
-                const SeqSpan sp = seq_span(p, b);
-                if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
-                cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, chunk);
-            }
-            int x = cnt;
-#pragma unroll
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(x, o, 64);
-                if (lane >= o) x += y;
-            }
-            if (lane == 63) s_wsum[wave] = x;
-            __syncthreads();
-            if (wave == 0) {
-                int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
-#pragma unroll
-                for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
-                    const int y = __shfl_up(w, o, 64);
-                    if (lane >= o) w += y;
-                }
-                if (lane < kPlanThreads / 64) s_wsum[lane] = w;
-            }
-            __syncthreads();
-            const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
-            if (b < p.batch) off[b] = carry + incl - cnt;
-            carry += s_wsum[kPlanThreads / 64 - 1];
-            __syncthreads();
-        }
-        if (attempt == 1 || !(split && p.chunk_adapt)) break;
-        {
-            const unsigned long long units = (unsigned long long)carry * (unsigned long long)p.Hk;
-            const unsigned long long slots = (unsigned long long)max(1, p.slots);
-            if (units <= slots && 2 * units >= slots) break;
-        }
+    if (split && p.chunk_adapt) {
+        // item counts of every candidate chunk in one pass over the sequences
+        // (spans staged in LDS on the way)
         if (tid < kChunkCands) s_cand[tid] = 0;
-        if (tid == 0) s_chunk = chunk;
         __syncthreads();
         unsigned long long cnt[kChunkCands] = {};
         for (int b = tid; b < p.batch; b += kPlanThreads) {
-            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+            const SeqSpan sp = seq_span(p, b);
+            if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             const int tiles = ceil_div(sp.Lq * p.G, R);
 #pragma unroll
             for (int k = 0; k < kChunkCands; ++k)
@@ -386,25 +346,65 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
             unsigned long long x = cnt[k];
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-            if (lane == 0) atomicAdd(&s_cand[k], x);
+            if (lane == 0 && x) atomicAdd(&s_cand[k], x);
         }
         __syncthreads();
-        if (tid == 0) {
-            const unsigned long long slots = (unsigned long long)max(1, p.slots);
-            unsigned long long best = ~0ull;
-            for (int k = 0; k < kChunkCands; ++k) {
-                const int c = chunk_cand(p, k);
-                const unsigned long long units = s_cand[k] * (unsigned long long)p.Hk;
-                const unsigned long long est = (units + slots - 1) / slots * (unsigned long long)(c + 2 * R + 64);
-                if (est < best) {
-                    best = est;
-                    s_chunk = c;
-                }
+        if (wave == 0) {  // one candidate per lane (unit counts < 2^31: checked on the host)
+            const unsigned slots = (unsigned)max(1, p.slots);
+            const unsigned ub = (unsigned)s_cand[kBaseCand] * (unsigned)p.Hk;
+            unsigned long long key = ~0ull;  // (estimate, candidate) of this lane
+            if (lane < kChunkCands) {
+                const unsigned units = (unsigned)s_cand[lane] * (unsigned)p.Hk;
+                const unsigned long long est = (unsigned long long)((units + slots - 1) / slots) *
+                                               (unsigned long long)(chunk_cand(p, lane) + 2 * R + 64);
+                key = (est << 4) | (unsigned long long)lane;
             }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const unsigned long long y = __shfl_xor(key, o, 64);
+                key = y < key ? y : key;
+            }
+            // a round that is at least half full keeps the base size
+            if (lane == 0) s_chunk = (ub <= slots && 2 * ub >= slots) ? chunk : chunk_cand(p, (int)(key & 15));
         }
         __syncthreads();
-        if (s_chunk == chunk) break;
         chunk = s_chunk;
+    }
+    const bool staged = split && p.chunk_adapt && cached;  // spans already in LDS
+
+    // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
+    // LDS step per 1024 sequences)
+    int carry = 0;
+    for (int base = 0; base < p.batch; base += kPlanThreads) {
+        const int b = base + tid;
+        int cnt = 0;
+        if (b < p.batch) {
+            const SeqSpan sp = staged ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+            if (cached && !staged) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
+            cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, chunk);
+        }
+        int x = cnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(x, o, 64);
+            if (lane >= o) x += y;
+        }
+        if (lane == 63) s_wsum[wave] = x;
+        __syncthreads();
+        if (wave == 0) {
+            int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
+#pragma unroll
+            for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
+                const int y = __shfl_up(w, o, 64);
+                if (lane >= o) w += y;
+            }
+            if (lane < kPlanThreads / 64) s_wsum[lane] = w;
+        }
+        __syncthreads();
+        const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
+        if (b < p.batch) off[b] = carry + incl - cnt;
+        carry += s_wsum[kPlanThreads / 64 - 1];
+        __syncthreads();
     }
     const int total = min(carry, p.items_bound);
     if (tid == 0) {
@@ -412,11 +412,22 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
         *p.item_count = total;
     }
     __syncthreads();
+    // split partials: chunks per token for the combine (0 = in no sequence); one
+    // token per thread, its sequence found by a search over the query offsets
     if (split)
-        for (int b = tid; b < p.batch; b += kPlanThreads) {
-            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-            const int nc = seq_chunks(p, sp.Lk, chunk);
-            for (int t = sp.q0; t < sp.q0 + sp.Lq; ++t) p.tok_nc[t] = nc;
+        for (int t = tid; t < p.total_q; t += kPlanThreads) {
+            int lo = 0, hi = p.batch;  // last b whose first query row is <= t
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                const int q0 = cached ? s_span[mid].x : seq_span(p, mid).q0;
+                if (q0 <= t) lo = mid; else hi = mid;
+            }
+            int nc = 0;
+            if (p.batch > 0) {
+                const SeqSpan sp = cached ? SeqSpan{s_span[lo].x, s_span[lo].y, s_span[lo].z, s_span[lo].w} : seq_span(p, lo);
+                if (t >= sp.q0 && t < sp.q0 + sp.Lq) nc = seq_chunks(p, sp.Lk, chunk);
+            }
+            p.tok_nc[t] = nc;
         }
 
     // decode item i -> (b, rt, c, nc, cost bucket); the first pass counts
@@ -454,13 +465,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
             }
         }
         __syncthreads();
-        if (pass == 0 && tid == 0) {  // bucket starts, most expensive first
-            int run = 0;
-            for (int k = kCostBuckets - 1; k >= 0; --k) {
-                const int cnt = s_hist[k];
-                s_hist[k] = run;
-                run += cnt;
+        if (pass == 0 && wave == 0) {  // bucket starts, most expensive first: one wave scan
+            static_assert(kCostBuckets == 128, "two buckets per lane");
+            const int k0 = kCostBuckets - 1 - 2 * lane;  // this lane's buckets k0, k0 - 1
+            const int c0 = s_hist[k0], c1 = s_hist[k0 - 1];
+            int x = c0 + c1;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
             }
+            const int excl = x - c0 - c1;
+            s_hist[k0] = excl;
+            s_hist[k0 - 1] = excl + c0;
         }
         __syncthreads();
     }
@@ -1089,7 +1106,10 @@ attn_fwd_kernel(const FwdParams p) {
     }
 }
 
-// Merge split partials: one wave per (token, head).
+// Merge split partials: one wave per (token, head).  Lane c holds chunk c's
+// weight 2^(lse_c - max); the partial rows are then accumulated four chunks at a
+// time so that several loads are in flight (a chunk-by-chunk loop waits twice
+// per chunk).
 template <class E, int DP>
 __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int lane = threadIdx.x & 63;
@@ -1102,8 +1122,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int64_t cstride_l = (int64_t)p.total_q * p.H;
     const int64_t b = p.padded ? t / p.uniform_q : 0;  // only padded calls have per-sequence offsets
     float* lse = p.lse ? p.lse + (int64_t)h * p.lse_sh + t + b * p.lse_bx : nullptr;
-    float M = kNegInf;
-    for (int c = lane; c < nc; c += 64) M = fmaxf(M, pl[c * cstride_l]);
+    const float l0 = lane < nc ? pl[lane * cstride_l] : kNegInf;  // the first 64 chunks
+    float M = l0;
+    for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, pl[c * cstride_l]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     uint16_t* orow = p.out + (int64_t)t * p.o_s0 + b * p.o_bx + (int64_t)h * p.o_s1;
@@ -1114,19 +1135,36 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
         return;
     }
     constexpr int PER = DP / 64;
+    constexpr int U = 4;  // chunks per group of loads
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     float wsum = 0.f;
-    const float* po = p.part_o + ((int64_t)t * p.H + h) * DP;
+    const float* po = p.part_o + ((int64_t)t * p.H + h) * DP + lane;
     const int64_t cstride_o = (int64_t)p.total_q * p.H * DP;
-    for (int c = 0; c < nc; ++c) {
-        const float w = __builtin_amdgcn_exp2f(pl[c * cstride_l] - M);
-        wsum += w;
-        if (w == 0.f) continue;
+    for (int c0 = 0; c0 < nc; c0 += 64) {
+        const int c = c0 + lane;
+        const float lc = c0 == 0 ? l0 : (c < nc ? pl[c * cstride_l] : kNegInf);
+        const float wl = c < nc ? __builtin_amdgcn_exp2f(lc - M) : 0.f;  // lane c's chunk weight
+        wsum += wl;
+        const int n = min(64, nc - c0);
+        for (int j = 0; j < n; j += U) {
+            float w[U], x[U][PER];
 #pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] += w * po[c * cstride_o + j * 64 + lane];
+            for (int q = 0; q < U; ++q) {
+                const int jj = min(j + q, n - 1);  // a short last group repeats a chunk with weight 0
+                w[q] = j + q < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
+#pragma unroll
+                for (int e = 0; e < PER; ++e) x[q][e] = po[(int64_t)(c0 + jj) * cstride_o + e * 64];
+            }
+#pragma unroll
+            for (int q = 0; q < U; ++q)
+#pragma unroll
+                for (int e = 0; e < PER; ++e) acc[e] += w[q] != 0.f ? w[q] * x[q][e] : 0.f;
+        }
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wsum += __shfl_xor(wsum, off, 64);
     const float inv = 1.f / wsum;
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
