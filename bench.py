@@ -130,8 +130,13 @@ def append_work(wl):
     return dict(total_new=int(total_new), row_bytes=rows, total_bytes=2.0 * rows + meta)
 
 
-def stored_traffic(workload: str, op: str = "fwd"):
-    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged."""
+def stored_traffic(workload: str, op: str = "fwd", dtype: str = "bf16", alibi: bool = False):
+    """HBM bytes per launch from the committed counter summary, if the kernel is unchanged.
+
+    The summaries were taken on the bf16 kernels without ALiBi slopes; other
+    instantiations (fp16, ALiBi) report None."""
+    if dtype != "bf16" or alibi:
+        return None
     if op == "append":
         path = os.path.join(ROOT, "profiles", "kv_append_%s_hbm_traffic.md" % workload)
         src = APPEND_SRC
@@ -356,7 +361,7 @@ def bench_append(args, fa, W, hip, dev, stream):
         assert torch.equal(vc.view(torch.int16).cpu(), wl.v.view(torch.int16)), "append changed the V pool"
     achieved = work["total_bytes"] / (kern_mean * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(args.workload, "append")}
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(args.workload, "append", args.dtype)}
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle append)", file=sys.stderr, flush=True)
@@ -650,7 +655,7 @@ def main(argv=None):
         achieved = work["flops"] / (kern_mean * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    traffic = stored_traffic(args.workload)
+    traffic = stored_traffic(args.workload, "fwd", args.dtype, args.alibi)
     roof["traffic"] = traffic
 
     cpu = None
