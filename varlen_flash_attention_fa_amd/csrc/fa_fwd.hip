@@ -454,7 +454,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 kb = max(kb, c * chunk);
                 ke = min(ke, (c + 1) * chunk);
             }
-            const int64_t cost = (int64_t)max(0, ke - kb) * (r1 - r0 + 1) + (r1 - r0 + 1);
+            // a tile costs its keys times the rows of its active waves (a wave
+            // with any row computes all MR of them; waves without rows skip the
+            // compute), plus about one wave's worth for the copies and barriers
+            const int nr = r1 - r0 + 1;
+            const int act = (nr + p.wave_rows - 1) / p.wave_rows * p.wave_rows;
+            const int64_t cost = (int64_t)max(0, ke - kb) * (act + p.wave_rows) + nr;
             const int bucket = cost_bucket(cost);
             if (pass == 0) {
                 atomicAdd(&s_hist[bucket], 1);
@@ -597,6 +602,9 @@ attn_fwd_kernel(const FwdParams p) {
         w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
         w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
     }
+    // a wave whose rows all lie past the item's last row (the last row tile of a
+    // sequence) only takes part in the copies and barriers
+    const bool wact = __ballot(row_ok) != 0;
 
     // Q^T operand: lane holds q[row][s*KSTEP + kgrp*8 .. +8) for every k-step s.
     // The softmax below needs a positive scale: a negative scale is applied as
@@ -663,7 +671,7 @@ attn_fwd_kernel(const FwdParams p) {
 
         // issue the copies of tile t of this segment into stage t % NS: which = 0
         // K only, 1 V only, 2 both
-        auto issue = [&](int t, int which) {
+        auto issue = [&](int t, int which) __attribute__((always_inline)) {
             const int ts = seg0 + t * BN;
             unsigned char* kbuf = smem + (t % NS) * 2 * TILEB;
             unsigned char* vbuf = kbuf + TILEB;
@@ -801,7 +809,25 @@ attn_fwd_kernel(const FwdParams p) {
                 if (t < ntiles) issue(t, 2);
         }
 
-        for (int t = 0; t < ntiles; ++t) {
+        // a wave without rows keeps the copies and barriers of the loop below
+        for (int t = 0; !wact && t < ntiles; ++t) {
+            if constexpr (NS == 1) {
+                wait_vmcnt<0>();
+                __syncthreads();
+                issue(t, 1);
+                __syncthreads();
+                if (t + 1 < ntiles) issue(t + 1, 0);
+                if (t + 1 < ntiles) wait_vmcnt<NI>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+            } else {
+                if (t + NS - 2 < ntiles) wait_vmcnt<(NS >= 2 ? (NS - 2) * 2 * NI : 0)>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                if (t + NS - 1 < ntiles) issue(t + NS - 1, 2);
+            }
+        }
+        for (int t = 0; wact && t < ntiles; ++t) {
             if constexpr (NS == 1) {
                 wait_vmcnt<0>();  // K(t) has landed (no other copy is in flight)
                 __syncthreads();  // K(t) visible to every wave; every wave is done with V(t-1)
@@ -1029,23 +1055,31 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                     for (int pat = 0; pat < NPAT; ++pat) vx[pat][h2] = bx ^ ((pat * CPD) << 4);
                 }
+                if constexpr (MR == 32) {
+                    // MFMA i: unit i / (2 NDB), 16-key half (i / NDB) % 2, d-block i % NDB;
+                    // fragments read PF MFMAs ahead (one MFMA is shorter than an LDS read)
+                    constexpr int NMF = NU * 2 * NDB, PF = 3;
+                    auto vread = [&](int i) {
+                        const int u = i / (2 * NDB), ts = (i / NDB) % 2, db = i % NDB;
+                        const int off = (u * 32 + ts * 16) * ROWB + (db / NPAT) * (NPAT * CPD * 16);
+                        const u32x2 lo2 = lds_read_tr16(vbuf + vx[db % NPAT][0] + off);
+                        const u32x2 hi2 = lds_read_tr16(vbuf + vx[db % NPAT][1] + off);
+                        return u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
+                    };
+                    u32x4 a[PF];
 #pragma unroll
-                for (int u = 0; u < NU; ++u) {
-                    if constexpr (MR == 32) {
+                    for (int i = 0; i < PF - 1; ++i) a[i] = vread(i);
 #pragma unroll
-                        for (int ts = 0; ts < 2; ++ts) {
-                            const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
-                                                  pk[u][ts * 4 + 3]};
+                    for (int i = 0; i < NMF; ++i) {
+                        if (i + PF - 1 < NMF) a[(i + PF - 1) % PF] = vread(i + PF - 1);
+                        const int u = i / (2 * NDB), ts = (i / NDB) % 2, db = i % NDB;
+                        const u32x4 b = u32x4{pk[u][ts * 4 + 0], pk[u][ts * 4 + 1], pk[u][ts * 4 + 2],
+                                              pk[u][ts * 4 + 3]};
+                        o[db] = M::mma(a[i % PF], b, o[db]);
+                    }
+                } else {
 #pragma unroll
-                            for (int db = 0; db < NDB; ++db) {
-                                const int off = (u * 32 + ts * 16) * ROWB + (db / NPAT) * (NPAT * CPD * 16);
-                                const u32x2 lo2 = lds_read_tr16(vbuf + vx[db % NPAT][0] + off);
-                                const u32x2 hi2 = lds_read_tr16(vbuf + vx[db % NPAT][1] + off);
-                                const u32x4 a = u32x4{lo2[0], lo2[1], hi2[0], hi2[1]};
-                                o[db] = M::mma(a, b, o[db]);
-                            }
-                        }
-                    } else {
+                    for (int u = 0; u < NU; ++u) {
                         const u32x4 b = u32x4{pk[u][0], pk[u][1], pk[u][2], pk[u][3]};
 #pragma unroll
                         for (int db = 0; db < NDB; ++db) {
@@ -1361,6 +1395,7 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     hipStream_t s = static_cast<hipStream_t>(stream);
     FwdParams p = p_in;
     p.rows = plan.rows;
+    p.wave_rows = plan.mr;
     p.items_bound = (int32_t)plan.items_bound;
     p.xcd_chunk = plan.xcd_chunk;
     p.chunk = plan.chunk;
