@@ -523,6 +523,22 @@ attn_fwd_kernel(const FwdParams p) {
     constexpr int RPI = 64 / CH > 0 ? 64 / CH : 1;   // rows per 64-lane copy
     constexpr int CPD = MR / 8;           // 16-byte chunks per d-block of the PV product
     constexpr int NPAT = (NDB < (SWV + 1) / CPD) ? NDB : (SWV + 1) / CPD;  // V read XOR patterns
+    // 16-byte chunk c of LDS row r sits at position c ^ swk(r) (K) or c ^ swv(r) (V).
+    // Both maps are linear over the row bits, so swz(r0 + l) = swz(r0) ^ swz(l) when r0
+    // is a multiple of a power of two above l.  With 32 rows per wave and >= 16 chunks
+    // per row: the K rows 0..15 that one operand read touches take 16 distinct
+    // positions, and rows r, r + 8 differ by 4 mod 8; the V rows 0..3 of a transposing
+    // read land in distinct 64-byte quarters and distinct 32-byte eighths mod 128 bytes.
+    // Either way the reads are free of bank conflicts whether the LDS serves 128 or 256
+    // bytes per cycle.  Other shapes keep row & 15 (K) and 2 row & 15 (V).
+    auto swk = [](int r) {
+        if constexpr (MR == 32 && CH >= 16) return (r & 15) ^ ((r >> 1) & 4);
+        else return r & SWK;
+    };
+    auto swv = [](int r) {
+        if constexpr (MR == 32 && CH >= 16) return (0xCA60 >> (4 * (r & 3))) & 15;  // 0, 6, 10, 12
+        else return (2 * r) & SWV;
+    };
     static_assert(BN % 32 == 0 && (BN * CH) % NT == 0 && CH <= 64 && 64 % CH == 0, "tile shape");
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * 2 * TILEB];
@@ -713,15 +729,15 @@ attn_fwd_kernel(const FwdParams p) {
                     kw = reinterpret_cast<const unsigned char*>(p.k + row * p.k_s0 + kbx + (int64_t)hk * p.k_s1);
                     vw = reinterpret_cast<const unsigned char*>(p.v + row * p.v_s0 + vbx + (int64_t)hk * p.v_s1);
                 }
-                const int xk = lpos ^ (lrow & SWK);
-                const int xv = lpos ^ ((2 * lrow) & SWV);
+                const int xk = lpos ^ swk(lrow);
+                const int xv = lpos ^ swv(lrow);
                 const unsigned lk_off = (unsigned)lrow * (unsigned)p.k_rowb;
                 const unsigned lv_off = (unsigned)lrow * (unsigned)p.v_rowb;
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int r0 = wv * W + i * RPI;  // tile row of the copy's first lane row (uniform)
-                    const unsigned vk = lk_off + ((unsigned)(xk ^ (r0 & SWK)) << 4);
-                    const unsigned vv = lv_off + ((unsigned)(xv ^ ((2 * r0) & SWV)) << 4);
+                    const unsigned vk = lk_off + ((unsigned)(xk ^ swk(r0)) << 4);
+                    const unsigned vv = lv_off + ((unsigned)(xv ^ swv(r0)) << 4);
                     const unsigned dst = smem_lds + (unsigned)((t % NS) * 2 * TILEB + (wv * NI + i) * 1024);
                     if (which != 1) copy16_to_lds_sv(kw + (size_t)(i * RPI) * p.k_rowb, vk, dst);
                     if (which != 0) copy16_to_lds_sv(vw + (size_t)(i * RPI) * p.v_rowb, vv, dst + TILEB);
@@ -752,8 +768,8 @@ attn_fwd_kernel(const FwdParams p) {
                         offk = (int64_t)(it.k0 + n) * p.k_s0 + kbx + (int64_t)hk * p.k_s1;
                         offv = (int64_t)(it.k0 + n) * p.v_s0 + vbx + (int64_t)hk * p.v_s1;
                     }
-                    int ck = lpos ^ (rr & SWK);
-                    int cv = lpos ^ ((2 * rr) & SWV);
+                    int ck = lpos ^ swk(rr);
+                    int cv = lpos ^ swv(rr);
                     ck = ck < nchv ? ck : 0;
                     cv = cv < nchv ? cv : 0;
                     const unsigned dst = smem_lds + (unsigned)__builtin_amdgcn_readfirstlane((t % NS) * 2 * TILEB + (wave * NI + i) * 1024);
@@ -779,8 +795,8 @@ attn_fwd_kernel(const FwdParams p) {
                         rowk = p.k + (int64_t)(it.k0 + nc) * p.k_s0 + kbx + (int64_t)hk * p.k_s1;
                         rowv = p.v + (int64_t)(it.k0 + nc) * p.v_s0 + vbx + (int64_t)hk * p.v_s1;
                     }
-                    const int ck = lpos ^ (rr & SWK);
-                    const int cv = lpos ^ ((2 * rr) & SWV);
+                    const int ck = lpos ^ swk(rr);
+                    const int cv = lpos ^ swv(rr);
                     const u32x4 zk = u32x4{0u, 0u, 0u, 0u};
                     if (which != 1) {
                         const u32x4 valk = ok ? load8(rowk, ck * 8, D, false) : zk;
@@ -856,7 +872,7 @@ attn_fwd_kernel(const FwdParams p) {
             if constexpr (MR == 32) {
                 const int ln = opaque_lane();
                 const int kr = kappa32(ln & 31);
-                const int kbase = kr * ROWB + (((ln >> 5) ^ (kr & SWK)) << 4);
+                const int kbase = kr * ROWB + (((ln >> 5) ^ swk(kr)) << 4);
                 auto kread = [&](int u, int st) {
                     return *reinterpret_cast<const u32x4*>(kbuf + (kbase ^ (st << 5)) + u * 32 * ROWB);
                 };
@@ -916,7 +932,7 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int sb = 0; sb < 2; ++sb) {
                     const int kr = (rl >> 2) * 8 + sb * 4 + (rl & 3);
-                    kbase[sb] = kr * ROWB + (((ln >> 4) ^ (kr & SWK)) << 4);
+                    kbase[sb] = kr * ROWB + (((ln >> 4) ^ swk(kr)) << 4);
                 }
                 auto kread = [&](int u, int sb, int st) {
                     return *reinterpret_cast<const u32x4*>(kbuf + (kbase[sb] ^ (st << 6)) + u * 32 * ROWB);
@@ -1051,7 +1067,7 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
                 for (int h2 = 0; h2 < 2; ++h2) {
                     const int rr = r0 + 4 * h2;
-                    const int bx = rr * ROWB + ((c0 ^ ((2 * rr) & SWV)) << 4) + (a16 & 1) * 8;
+                    const int bx = rr * ROWB + ((c0 ^ swv(rr)) << 4) + (a16 & 1) * 8;
 #pragma unroll
                     for (int pat = 0; pat < NPAT; ++pat) vx[pat][h2] = bx ^ ((pat * CPD) << 4);
                 }
