@@ -497,15 +497,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
 template <class E, int DP, int MR, int WR, int BN, int NS, bool AL>
-// Waves per SIMD asked of the compiler: three for the D<=128 prefill kernel
-// without ALiBi (its 33 KiB of LDS allow three workgroups per CU; the staggered
-// K/V copies would otherwise raise it to 193 registers and two waves; at 168 a
-// few values that live across the tile loop spill, outside the loop); two for
+// Waves per SIMD asked of the compiler: three for the D<=128 prefill kernels,
+// with or without ALiBi (their 33 KiB of LDS allow three workgroups per CU; the
+// staggered K/V copies would otherwise raise them to 181-193 registers and two
+// waves; at 168 a few values that live across the tile loop spill, outside the
+// loop, and the ALiBi one reloads two per tile); two for
 // the other 4-wave D<=128 kernels and the 4-wave D256/D512 decode kernels (the
 // D512 one would otherwise take 380 registers and keep one wave per SIMD where
 // its 64 KiB of LDS allow two workgroups per CU).
 __global__ __launch_bounds__(64 * WR) __attribute__((amdgpu_waves_per_eu(
-    (WR == 4 && DP <= 128 && MR == 32 && !AL) ? 3 : ((WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256)) ? 2 : 1, 8))) void
+    (WR == 4 && DP <= 128 && MR == 32) ? 3 : ((WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256)) ? 2 : 1, 8))) void
 attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR, E> M;
     typedef typename M::acc_t acc_t;
