@@ -531,13 +531,19 @@ attn_fwd_kernel(const FwdParams p) {
     // positions, and rows r, r + 8 differ by 4 mod 8; the V rows 0..3 of a transposing
     // read land in distinct 64-byte quarters and distinct 32-byte eighths mod 128 bytes.
     // Either way the reads are free of bank conflicts whether the LDS serves 128 or 256
-    // bytes per cycle.  Other shapes keep row & 15 (K) and 2 row & 15 (V).
+    // bytes per cycle.
+    // With 16 rows per wave, one K operand read touches rows {0..3, 8..11, 16..19,
+    // 24..27} (+ 4), which take 16 distinct positions; the V rows 0..3 and 8..11
+    // of a transposing read take distinct 32-byte segments.  Rows of fewer than 16
+    // chunks keep row & (chunks - 1) (K) and 2 row & (chunks - 1) (V).
     auto swk = [](int r) {
         if constexpr (MR == 32 && CH >= 16) return (r & 15) ^ ((r >> 1) & 4);
+        else if constexpr (CH >= 16) return (r & 3) | ((r >> 1) & 12);
         else return r & SWK;
     };
     auto swv = [](int r) {
         if constexpr (MR == 32 && CH >= 16) return (0xCA60 >> (4 * (r & 3))) & 15;  // 0, 6, 10, 12
+        else if constexpr (CH >= 16) return ((2 * r) & 6) | (r & 8);
         else return (2 * r) & SWV;
     };
     static_assert(BN % 32 == 0 && (BN * CH) % NT == 0 && CH <= 64 && 64 % CH == 0, "tile shape");
