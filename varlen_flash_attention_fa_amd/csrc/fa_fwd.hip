@@ -454,12 +454,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 kb = max(kb, c * chunk);
                 ke = min(ke, (c + 1) * chunk);
             }
-            // a tile costs its keys times the rows of its active waves (a wave
-            // with any row computes all MR of them; waves without rows skip the
-            // compute), plus about one wave's worth for the copies and barriers
+            // every wave of the workgroup computes all its rows for every key tile,
+            // so a partial row tile costs as much as a full one: the keys decide
+            // (rows only break ties)
             const int nr = r1 - r0 + 1;
-            const int act = (nr + p.wave_rows - 1) / p.wave_rows * p.wave_rows;
-            const int64_t cost = (int64_t)max(0, ke - kb) * (act + p.wave_rows) + nr;
+            const int64_t cost = (int64_t)max(0, ke - kb) * R + nr;
             const int bucket = cost_bucket(cost);
             if (pass == 0) {
                 atomicAdd(&s_hist[bucket], 1);
@@ -625,9 +624,6 @@ attn_fwd_kernel(const FwdParams p) {
         w_lo = max(w_lo, __shfl_xor(w_lo, off, 64));
         w_hi = min(w_hi, __shfl_xor(w_hi, off, 64));
     }
-    // a wave whose rows all lie past the item's last row (the last row tile of a
-    // sequence) only takes part in the copies and barriers
-    const bool wact = __ballot(row_ok) != 0;
 
     // Q^T operand: lane holds q[row][s*KSTEP + kgrp*8 .. +8) for every k-step s.
     // The softmax below needs a positive scale: a negative scale is applied as
@@ -832,25 +828,7 @@ attn_fwd_kernel(const FwdParams p) {
                 if (t < ntiles) issue(t, 2);
         }
 
-        // a wave without rows keeps the copies and barriers of the loop below
-        for (int t = 0; !wact && t < ntiles; ++t) {
-            if constexpr (NS == 1) {
-                wait_vmcnt<0>();
-                __syncthreads();
-                issue(t, 1);
-                __syncthreads();
-                if (t + 1 < ntiles) issue(t + 1, 0);
-                if (t + 1 < ntiles) wait_vmcnt<NI>();
-                else wait_vmcnt<0>();
-                __syncthreads();
-            } else {
-                if (t + NS - 2 < ntiles) wait_vmcnt<(NS >= 2 ? (NS - 2) * 2 * NI : 0)>();
-                else wait_vmcnt<0>();
-                __syncthreads();
-                if (t + NS - 1 < ntiles) issue(t + NS - 1, 2);
-            }
-        }
-        for (int t = 0; wact && t < ntiles; ++t) {
+        for (int t = 0; t < ntiles; ++t) {
             if constexpr (NS == 1) {
                 wait_vmcnt<0>();  // K(t) has landed (no other copy is in flight)
                 __syncthreads();  // K(t) visible to every wave; every wave is done with V(t-1)
@@ -1418,7 +1396,6 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     hipStream_t s = static_cast<hipStream_t>(stream);
     FwdParams p = p_in;
     p.rows = plan.rows;
-    p.wave_rows = plan.mr;
     p.items_bound = (int32_t)plan.items_bound;
     p.xcd_chunk = plan.xcd_chunk;
     p.chunk = plan.chunk;

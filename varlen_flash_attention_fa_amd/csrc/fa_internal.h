@@ -36,7 +36,6 @@ struct FwdParams {
     int32_t slots;          // workgroups of the main kernel resident at once (whole GPU)
     int32_t max_chunks;
     int32_t rows;           // rows per work item (MFMA rows per wave * waves)
-    int32_t wave_rows;      // MFMA rows per wave
     int32_t items_bound;    // upper bound of the number of work items per K/V head
     int32_t xcd_chunk;      // work units per run on one XCD (grid remap)
     int4* items;            // work list: per item {b, rt, c | nc<<16, 0}, {q0, Lq, k0, Lk}
