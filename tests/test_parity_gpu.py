@@ -97,6 +97,15 @@ def test_forced_split_sizes(oracle_mod, force_env, split):
     check(oracle_mod, wl, "split %d" % split)
 
 
+def test_prefill_short_list_splits_keys(oracle_mod):
+    # a few row tiles over long key ranges: the plan cuts the keys into chunks
+    # (merged by the combine kernel) without any forcing
+    wl = W.make_custom([64, 9], [20000, 9000], 8, 2, 128, seed=17, page=64, poison=True)
+    check(oracle_mod, wl, "auto split paged")
+    wl = W.make_custom([100], [16500], 8, 1, 64, seed=18, window_left=5000)
+    check(oracle_mod, wl, "auto split window")
+
+
 # --------------------------------------------------------------- edge cases
 
 def test_empty_and_degenerate_sequences(oracle_mod):

@@ -1322,15 +1322,18 @@ int make_plan(const Shapes& s, Plan* plan) {
         P.chunk_min = INT_MAX;
         P.adapt = false;
         P.max_chunks = 1;
-        // Few row tiles over long key ranges (chunked prefill on a long cache) give
-        // too few, too uneven work items for the chip: cut the keys into halves of
-        // the longest range (at least 4096 keys), merged by the combine kernel.
-        // Smaller chunks balance better but their partials cost more than they save.
+        // Only a work list too short to fill one round of resident workgroups
+        // (a few row tiles over long key ranges) has its keys cut into chunks,
+        // merged by the combine kernel: about 1536 work units in all, chunks of at
+        // least 2048 keys.  Longer lists are balanced by the planner's
+        // largest-first order alone; splitting them only adds partials and the
+        // combine (a 16-sequence chunked prefill over 8k-key caches: 0.37 ms with
+        // halves, 0.35 ms without).
         const int64_t rows = (int64_t)P.mr * P.wr;
         const int64_t items = ((s.total_q * G + rows - 1) / rows + s.batch) * s.Hk;
         int64_t chunk = 0;
-        if (items < 3072 && s.max_lk >= 8192)
-            chunk = std::max<int64_t>(4096, (s.max_lk / 2 + P.bn - 1) / P.bn * P.bn);
+        if (items < 512 && s.max_lk >= 8192)
+            chunk = std::max<int64_t>(2048, (s.max_lk * items / 1536 + P.bn - 1) / P.bn * P.bn);
         chunk = env_int("FA_SPLIT_KEYS", (int)chunk);
         if (chunk > 0) {
             chunk = std::max<int64_t>(P.bn, (chunk + P.bn - 1) / P.bn * P.bn);
