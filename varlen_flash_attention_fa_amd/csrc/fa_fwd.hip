@@ -271,8 +271,8 @@ __device__ __forceinline__ SeqSpan seq_span(const FwdParams& p, int b) {
 //
 // One workgroup turns cu_seqlens into the work list of the main kernel:
 // sequence b owns ceil(Lq_b*G/R) row tiles times nc_b key chunks.  Items are
-// written in decreasing order of estimated cost (rows x visible keys, in
-// half-octave buckets); the main kernel's workgroup x handles item x, and
+// written in decreasing order of estimated cost (visible keys x the workgroup's
+// rows, in half-octave buckets); the main kernel's workgroup x handles item x, and
 // workgroups are dispatched in index order, so the longest items start first
 // and the short ones fill the tail.
 constexpr int kPlanThreads = 1024;
@@ -1041,7 +1041,7 @@ attn_fwd_kernel(const FwdParams p) {
             // ---- O^T += V^T P^T, V^T slices by transposing LDS reads.  Per tile, the
             // lane's two read addresses (rows r0, r0 + 4) are built for the first 16
             // keys and each XOR pattern of the swizzled chunk bits; other 16-key
-            // groups add whole rows (the swizzle depends on the row mod 8 only) and
+            // groups add whole rows (the swizzle depends on the row mod 16 only) and
             // d-blocks past the swizzled bits add a whole chunk group, both constants.
             {
                 const int ln = opaque_lane();
