@@ -238,6 +238,20 @@ def test_workspace_bytes(lib):
     assert e.value.status == "FA_ERR_SHAPE"
 
 
+def test_prefill_split_only_for_short_work_lists(lib):
+    # the plan cuts prefill keys into chunks (split partials in the workspace)
+    # only when the work list cannot fill the GPU: a few row tiles over long keys
+    bt_long = desc([2, 313], dtype=FA_DTYPE_I32)                     # up to 20032 keys per sequence
+    pool = desc([700, 64, 2, 128])
+    short = fa.fa_varlen_workspace_bytes(desc([73, 8, 128]), pool, pool, 2, bt_long, 64)
+    assert short >= 73 * 8 * 129 * 4 * 2  # at least two chunks of fp32 partials
+    # a 16-sequence chunked prefill over 8k-key caches (about 1.2k work units): no split
+    bt_c3 = desc([16, 136], dtype=FA_DTYPE_I32)
+    pool3 = desc([2400, 64, 8, 128])
+    c3 = fa.fa_varlen_workspace_bytes(desc([4104, 32, 128]), pool3, pool3, 16, bt_c3, 64)
+    assert 0 < c3 < 4104 * 32 * 129 * 4
+
+
 # ------------------------------------------------------------ paged append
 
 KN = desc([6, 2, 64])
