@@ -305,6 +305,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     __shared__ int4 s_span[kLdsSeqs];
     __shared__ int s_wsum[kPlanThreads / 64];
     __shared__ int s_hist[kCostBuckets];
+    __shared__ int s_wcnt[kPlanThreads / 64][kCostBuckets];  // per-wave bucket counts of a chunk
     __shared__ unsigned long long s_cand[kChunkCands];
     __shared__ int s_chunk;
     const int tid = threadIdx.x;
@@ -315,6 +316,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     const int R = p.rows;
 
     for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_hist[i] = 0;
+    for (int i = tid; i < kCostBuckets * (kPlanThreads / 64); i += kPlanThreads) (&s_wcnt[0][0])[i] = 0;
 
     // Chunk size.  Work items of one call cost about the same, and the hardware
     // runs `slots` of them at a time, so the kernel takes about
@@ -431,42 +433,78 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
         }
 
     // decode item i -> (b, rt, c, nc, cost bucket); the first pass counts
-    // buckets, the second places each item at its bucket's next slot
+    // buckets, the second places each item in its bucket in item order (a stable
+    // counting sort: sequence, row tile, chunk), so that the workgroups running
+    // together on an XCD take neighbouring row tiles of one sequence and share
+    // its K/V window in that XCD's L2
     for (int pass = 0; pass < 2; ++pass) {
-        for (int i = tid; i < total; i += kPlanThreads) {
-            int lo = 0, hi = p.batch;  // last b with off[b] <= i
-            while (hi - lo > 1) {
-                const int mid = (lo + hi) >> 1;
-                if (off[mid] <= i) lo = mid; else hi = mid;
+        for (int base = 0; base < total; base += kPlanThreads) {
+            const int i = base + tid;
+            int bucket = -1;
+            int4 rec0 = {}, rec1 = {};
+            if (i < total) {
+                int lo = 0, hi = p.batch;  // last b with off[b] <= i
+                while (hi - lo > 1) {
+                    const int mid = (lo + hi) >> 1;
+                    if (off[mid] <= i) lo = mid; else hi = mid;
+                }
+                const int b = lo;
+                const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+                const int lq = sp.Lq, lk = sp.Lk;
+                const int nc = seq_chunks(p, lk, chunk);
+                const int local = i - off[b];
+                const int rt = local / nc, c = local % nc;
+                const int nrows = lq * p.G;
+                const int r0 = rt * R, r1 = min(nrows, r0 + R) - 1;
+                const Range a = row_range(p, r0 / p.G, lq, lk);
+                const Range z = row_range(p, r1 / p.G, lq, lk);
+                int kb = a.lo, ke = z.hi;
+                if (split) {
+                    kb = max(kb, c * chunk);
+                    ke = min(ke, (c + 1) * chunk);
+                }
+                // every wave of the workgroup computes all its rows for every key tile,
+                // so a partial row tile costs as much as a full one: the keys decide
+                // (rows only break ties)
+                const int nr = r1 - r0 + 1;
+                const int64_t cost = (int64_t)max(0, ke - kb) * R + nr;
+                bucket = cost_bucket(cost);
+                rec0 = make_int4(b, rt, c | (nc << 16), chunk);
+                rec1 = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             }
-            const int b = lo;
-            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-            const int lq = sp.Lq, lk = sp.Lk;
-            const int nc = seq_chunks(p, lk, chunk);
-            const int local = i - off[b];
-            const int rt = local / nc, c = local % nc;
-            const int nrows = lq * p.G;
-            const int r0 = rt * R, r1 = min(nrows, r0 + R) - 1;
-            const Range a = row_range(p, r0 / p.G, lq, lk);
-            const Range z = row_range(p, r1 / p.G, lq, lk);
-            int kb = a.lo, ke = z.hi;
-            if (split) {
-                kb = max(kb, c * chunk);
-                ke = min(ke, (c + 1) * chunk);
-            }
-            // every wave of the workgroup computes all its rows for every key tile,
-            // so a partial row tile costs as much as a full one: the keys decide
-            // (rows only break ties)
-            const int nr = r1 - r0 + 1;
-            const int64_t cost = (int64_t)max(0, ke - kb) * R + nr;
-            const int bucket = cost_bucket(cost);
             if (pass == 0) {
-                atomicAdd(&s_hist[bucket], 1);
-            } else {
-                const int pos = atomicAdd(&s_hist[bucket], 1);
-                p.items[2 * pos] = make_int4(b, rt, c | (nc << 16), chunk);
-                p.items[2 * pos + 1] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
+                if (bucket >= 0) atomicAdd(&s_hist[bucket], 1);
+                continue;
             }
+            // rank among the earlier items of this wave with the same bucket (one
+            // round per distinct bucket in the wave), and the wave's count per bucket
+            int rank = 0;
+            unsigned long long rem = __ballot(bucket >= 0);
+            while (rem) {
+                const int leader = __ffsll((long long)rem) - 1;
+                const int v = __shfl(bucket, leader, 64);
+                const unsigned long long m = __ballot(bucket == v);
+                if (bucket == v) rank = __popcll(m & ((1ull << lane) - 1ull));
+                if (lane == leader) s_wcnt[wave][v] = __popcll(m);
+                rem &= ~m;
+            }
+            __syncthreads();
+            if (bucket >= 0) {
+                int pos = s_hist[bucket] + rank;
+                for (int w = 0; w < wave; ++w) pos += s_wcnt[w][bucket];
+                p.items[2 * pos] = rec0;
+                p.items[2 * pos + 1] = rec1;
+            }
+            __syncthreads();
+            if (tid < kCostBuckets) {  // next chunk starts after this one's items
+                int sum = 0;
+                for (int w = 0; w < kPlanThreads / 64; ++w) {
+                    sum += s_wcnt[w][tid];
+                    s_wcnt[w][tid] = 0;
+                }
+                s_hist[tid] += sum;
+            }
+            __syncthreads();
         }
         __syncthreads();
         if (pass == 0 && wave == 0) {  // bucket starts, most expensive first: one wave scan
