@@ -318,26 +318,66 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_hist[i] = 0;
     for (int i = tid; i < kCostBuckets * (kPlanThreads / 64); i += kPlanThreads) (&s_wcnt[0][0])[i] = 0;
 
+    // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
+    // LDS step per 1024 sequences); returns the item count.  The first call stages
+    // the sequence spans in LDS (when they fit).
+    auto offsets = [&](int ck, bool staged) {
+        int carry = 0;
+        for (int base = 0; base < p.batch; base += kPlanThreads) {
+            const int b = base + tid;
+            int cnt = 0;
+            if (b < p.batch) {
+                const SeqSpan sp = staged ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+                if (cached && !staged) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
+                cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, ck);
+            }
+            int x = cnt;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o, 64);
+                if (lane >= o) x += y;
+            }
+            if (lane == 63) s_wsum[wave] = x;
+            __syncthreads();
+            if (wave == 0) {
+                int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
+#pragma unroll
+                for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
+                    const int y = __shfl_up(w, o, 64);
+                    if (lane >= o) w += y;
+                }
+                if (lane < kPlanThreads / 64) s_wsum[lane] = w;
+            }
+            __syncthreads();
+            const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
+            if (b < p.batch) off[b] = carry + incl - cnt;
+            carry += s_wsum[kPlanThreads / 64 - 1];
+            __syncthreads();
+        }
+        return carry;
+    };
     // Chunk size.  Work items of one call cost about the same, and the hardware
     // runs `slots` of them at a time, so the kernel takes about
-    // ceil(items / slots) rounds of (chunk + per-item overhead).  When the base
-    // chunk needs more than one round, or fills less than half of one, the
-    // candidate chunk with the smallest such estimate is taken and the items are
-    // counted again: fewer keys per item can fill the last round instead of
-    // leaving it nearly empty, more keys per item can save a round, and an
-    // underfilled round gains parallelism from smaller items.  A round that is at
-    // least half full already streams K/V at full bandwidth, and smaller chunks
-    // would only add partials, so the base chunk stays.
+    // ceil(items / slots) rounds of (chunk + per-item overhead).  The items are
+    // counted with the base chunk first; only when they need more than one round,
+    // or fill less than a quarter of one, are the candidates counted and the one
+    // with the smallest such estimate taken (fewer keys per item can fill the
+    // last round instead of leaving it nearly empty, more keys per item can save
+    // a round, and a nearly empty round gains parallelism from smaller items).
+    // A round that is at least a quarter full keeps the base chunk: a paged
+    // decode batch at half a round ran 98 us with it against 100 us with the
+    // candidate, and counting the candidates took 5 us of planner time.
     int chunk = p.chunk;
-    if (split && p.chunk_adapt) {
+    int carry = offsets(chunk, false);
+    const unsigned slots = (unsigned)max(1, p.slots);
+    const unsigned base_units = (unsigned)carry * (unsigned)p.Hk;
+    if (split && p.chunk_adapt && (base_units > slots || 4u * base_units < slots)) {
         // item counts of every candidate chunk in one pass over the sequences
-        // (spans staged in LDS on the way)
         if (tid < kChunkCands) s_cand[tid] = 0;
         __syncthreads();
         unsigned long long cnt[kChunkCands] = {};
         for (int b = tid; b < p.batch; b += kPlanThreads) {
-            const SeqSpan sp = seq_span(p, b);
-            if (cached) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
+            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
             const int tiles = ceil_div(sp.Lq * p.G, R);
 #pragma unroll
             for (int k = 0; k < kChunkCands; ++k)
@@ -352,8 +392,6 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
         }
         __syncthreads();
         if (wave == 0) {  // one candidate per lane (unit counts < 2^31: checked on the host)
-            const unsigned slots = (unsigned)max(1, p.slots);
-            const unsigned ub = (unsigned)s_cand[kBaseCand] * (unsigned)p.Hk;
             unsigned long long key = ~0ull;  // (estimate, candidate) of this lane
             if (lane < kChunkCands) {
                 const unsigned units = (unsigned)s_cand[lane] * (unsigned)p.Hk;
@@ -366,47 +404,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 const unsigned long long y = __shfl_xor(key, o, 64);
                 key = y < key ? y : key;
             }
-            // a round that is at least half full keeps the base size
-            if (lane == 0) s_chunk = (ub <= slots && 2 * ub >= slots) ? chunk : chunk_cand(p, (int)(key & 15));
+            if (lane == 0) s_chunk = chunk_cand(p, (int)(key & 15));
         }
         __syncthreads();
         chunk = s_chunk;
-    }
-    const bool staged = split && p.chunk_adapt && cached;  // spans already in LDS
-
-    // items per sequence -> exclusive offsets off[0..batch] (wave shuffles + one
-    // LDS step per 1024 sequences)
-    int carry = 0;
-    for (int base = 0; base < p.batch; base += kPlanThreads) {
-        const int b = base + tid;
-        int cnt = 0;
-        if (b < p.batch) {
-            const SeqSpan sp = staged ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-            if (cached && !staged) s_span[b] = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
-            cnt = ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, chunk);
-        }
-        int x = cnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(x, o, 64);
-            if (lane >= o) x += y;
-        }
-        if (lane == 63) s_wsum[wave] = x;
-        __syncthreads();
-        if (wave == 0) {
-            int w = lane < kPlanThreads / 64 ? s_wsum[lane] : 0;
-#pragma unroll
-            for (int o = 1; o < kPlanThreads / 64; o <<= 1) {
-                const int y = __shfl_up(w, o, 64);
-                if (lane >= o) w += y;
-            }
-            if (lane < kPlanThreads / 64) s_wsum[lane] = w;
-        }
-        __syncthreads();
-        const int incl = x + (wave > 0 ? s_wsum[wave - 1] : 0);
-        if (b < p.batch) off[b] = carry + incl - cnt;
-        carry += s_wsum[kPlanThreads / 64 - 1];
-        __syncthreads();
+        if (chunk != p.chunk) carry = offsets(chunk, cached);
     }
     const int total = min(carry, p.items_bound);
     if (tid == 0) {
