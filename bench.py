@@ -1,24 +1,42 @@
 #!/usr/bin/env python3
 """Benchmark of the varlen (paged) flash-attention forward on one MI355X.
 
-One step = one ``fa_varlen_fwd`` call (every kernel of the path) over one batch
-of seeded synthetic inputs already resident in HBM.  The default workload is
-the paged decode batch (64 sequences, q_len 1, kv lens U[1,4096], page 32,
-H 32 / Hk 8, head_dim 128), reported as KV GB/s; ``--workload`` selects the
-others (prefill ones are reported as TFLOP/s).
+One step = one ``fa_varlen_fwd`` call (every kernel of the path: planner,
+attention, split combine) over one batch of seeded synthetic inputs already
+resident in HBM.
+
+Default run (no ``--workload``): the headline is the long-prefill workload
+(8 sequences log-uniform in [1024, 16384] summing to 65,536 tokens, H 64 /
+Hk 8, head_dim 128, causal with window_left 4096), reported as TFLOP/s against
+the bf16 MFMA peak.  The same process then times the four other workloads
+under the ``suite`` key: paged decode (64 x q_len 1, kv U[1,4096], page 32,
+H 32 / Hk 8, D 128) and the two spec-decode workloads (32 x q_len 4, kv
+U[1024,32768], page 128, D 256 MHA and D 512 MQA) as KV GB/s against HBM, and
+paged chunked prefill (16 seqs, q U[1,512] over prefixes U[0,8192], page 64)
+as TFLOP/s.  ``--workload cN`` times one workload alone.
 
 Timed region: W untimed warm-up steps, then exactly K steps bracketed by
 ``torch.cuda.synchronize()``.  Consecutive steps read different copies of the
 inputs (enough copies to exceed the 256 MB last-level cache), so K/V really
-come from HBM.  The main kernel's own duration is read live with HIP events
-that the library records around it on its launch stream
-(``fa_varlen_set_kernel_events``), on every N-th timed step (``--event-every``,
-default 8): an event record costs a few microseconds of stream time.
+come from HBM.  Each entry reports two roofline fractions: ``frac`` for the
+attention kernel alone (its duration from HIP events that the library records
+around it on its launch stream, ``fa_varlen_set_kernel_events``, on every N-th
+timed step) and ``frac_call`` for the whole call (events around everything
+the call launches).
+
+Counters (default run; ``--no-counters`` skips them): before it touches the
+GPU, the bench runs itself three times under ``rocprofv3 --pmc`` (a short run
+of the headline workload preceded by a 1 GiB device copy):
+  * SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, ... -> counter-derived MFMA
+    utilisation of the attention kernel (busy MFMA cycles / (GPU cycles x
+    SIMDs)), the shader clock it ran at, and MFMA work issued vs algorithmic;
+  * FETCH_SIZE, then WRITE_SIZE -> the kernel's HBM bytes per launch, each
+    scaled by what the same counter reads for the 1 GiB copy (``traffic``).
 
 Prints ONE JSON line: metric/value/unit, ms_per_step, a ``roofline`` object
-for the main kernel (algorithmic bytes or FLOP per launch / its mean duration
-vs. the chip's peak) and a ``cpu_baseline`` object (the fp64 oracle timed on a
-bounded sample of the same workload on this host's cores).
+for the headline's attention kernel, ``cpu_baseline`` (the fp64 oracle timed on
+a bounded sample of the headline workload on this host's cores), ``suite``
+and ``counters``.
 
 ``--op append`` times the paged K/V append instead (``fa_kv_append``): each
 sequence of a paged workload appends as many new tokens as it has query rows
@@ -220,9 +238,9 @@ def cpu_baseline(wl, work, decode: bool, alibi=None):
     threads = oracle.default_threads()
     H, D = wl.num_heads, wl.head_dim
     fma_per_pair = 2.0 * D * H           # q.k and p.v, per head
-    # the oracle runs ~0.4 G fp64 multiply-adds per second per thread: this bounds
-    # the sample to roughly 10 s of wall time on the host cores
-    budget = 4.0e9 * threads
+    # the oracle runs ~1.5 G fp64 multiply-adds per second per thread (measured on
+    # 16 host cores): this bounds the sample to roughly 10-15 s of wall time
+    budget = 2.0e10 * threads
     if decode:
         # whole sequences until the budget: metric is KV bytes of the sequences served
         order = list(range(wl.batch))
@@ -240,11 +258,11 @@ def cpu_baseline(wl, work, decode: bool, alibi=None):
             spent += cost
             nseq += 1
         reps, t0 = 0, time.perf_counter()
-        while True:  # repeat a small sample until the timing is at least ~3 s long
+        while True:  # repeat a small sample until the timing is at least ~10 s long
             oracle.attention_workload(wl, token_sel=sel, nthreads=threads, alibi_slopes=alibi)
             reps += 1
             dt = time.perf_counter() - t0
-            if dt >= 3.0:
+            if dt >= 10.0:
                 break
         return {"value": round(reps * kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
                 "kind": "oracle",
@@ -271,7 +289,7 @@ def cpu_baseline(wl, work, decode: bool, alibi=None):
 # ------------------------------------------------------------- append bench
 
 def cpu_append_baseline(wl, k_new, v_new, work):
-    """Time the oracle's append of the whole workload, repeated for >= 3 s."""
+    """Time the oracle's append of the whole workload, repeated for >= 10 s."""
     import oracle
     oracle.build()
     reps, t0 = 0, time.perf_counter()
@@ -279,7 +297,7 @@ def cpu_append_baseline(wl, k_new, v_new, work):
         oracle.kv_append(k_new, v_new, wl.cu_seqlens_q, wl.cu_seqlens_k, wl.block_table, wl.k, wl.v)
         reps += 1
         dt = time.perf_counter() - t0
-        if dt >= 3.0:
+        if dt >= 10.0:
             break
     return {"value": round(reps * work["total_bytes"] / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
             "kind": "oracle",
@@ -498,15 +516,285 @@ def bench_padded(args, fa, W, hip, dev, stream):
     return 0
 
 
+# ------------------------------------------------------------ counter passes
+
+# one rocprofv3 --pmc run each (SQ: at most 8 counters, GRBM 2, TCC 4 per run)
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
+                 "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
+                 "GRBM_GUI_ACTIVE"]
+COUNTER_PASSES = [("mfma", MFMA_COUNTERS), ("fetch", ["FETCH_SIZE"]), ("write", ["WRITE_SIZE"])]
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+COPY_MIB = 1024
+XCDS = 8          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
+SIMDS_PER_CU = 4
+
+
+def _rocprofv3():
+    import shutil
+    for c in (shutil.which("rocprofv3"), "/opt/rocm/bin/rocprofv3"):
+        if c and os.path.exists(c):
+            return c
+    return None
+
+
+def parse_counter_csv(path):
+    """{kernel name: {counter: [per-dispatch values]}} and per-dispatch durations (ns)."""
+    import csv
+    vals, durs = {}, {}
+    for r in csv.DictReader(open(path)):
+        k = r["Kernel_Name"]
+        vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        durs.setdefault(k, {})[r["Dispatch_Id"]] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    return vals, {k: list(v.values()) for k, v in durs.items()}
+
+
+def _mean_tail(xs):
+    """Mean over the dispatches after the first (the first one runs on a cold cache)."""
+    xs = list(xs)
+    return float(np.mean(xs[1:] if len(xs) > 1 else xs))
+
+
+def run_counter_passes(workload, dtype, outroot, timeout_s=170):
+    """Run the counter passes as child processes; returns raw per-pass results or an error."""
+    prof = _rocprofv3()
+    if prof is None:
+        return {"error": "rocprofv3 not found"}
+    res = {"workload": workload, "passes": {}, "commands": []}
+    for name, counters in COUNTER_PASSES:
+        d = os.path.join(outroot, name)
+        os.makedirs(d, exist_ok=True)
+        cmd = ["timeout", "-s", "KILL", str(timeout_s), prof, "--pmc"] + counters + [
+            "--output-format", "csv", "-d", d, "-o", "run", "--", sys.executable,
+            os.path.join(ROOT, "bench.py"), "--counter-child", "--workload", workload, "--dtype", dtype,
+            "--steps", "3", "--warmup", "1"]
+        res["commands"].append(" ".join(cmd[4:]))
+        print("bench: counter pass %s (%s)" % (name, " ".join(counters)), file=sys.stderr, flush=True)
+        env = dict(os.environ, FA_BENCH_CHILD="1")
+        import subprocess
+        with open(os.path.join(d, "child.log"), "w") as log:
+            rc = subprocess.call(cmd, stdout=log, stderr=subprocess.STDOUT, env=env, cwd=ROOT)
+        csvp = os.path.join(d, "run_counter_collection.csv")
+        if not os.path.exists(csvp):
+            return dict(res, error="pass %s: no counter file (exit %d)" % (name, rc))
+        # rocprofv3 may exit non-zero after the program has finished and written
+        # complete results; the file is checked instead
+        res["passes"][name] = parse_counter_csv(csvp)
+    return res
+
+
+def derive_counters(raw, kname, alg_flops, alg_bytes, cus):
+    """Counter-derived figures of one kernel from the three passes."""
+    if "error" in raw:
+        return {"error": raw["error"]}
+    out = {"kernel": None}
+    mv, md = raw["passes"]["mfma"]
+    names = [k for k in mv if kname in k]
+    if not names:
+        return {"error": "%s not in the counter file" % kname}
+    k = names[0]
+    out["kernel"] = k
+    c = {n: _mean_tail(v) for n, v in mv[k].items()}
+    dur_ns = _mean_tail(md[k])
+    simds = cus * SIMDS_PER_CU
+    cycles = c["GRBM_GUI_ACTIVE"] / XCDS
+    out.update({
+        "dispatches": len(md[k]),
+        "profiled_kernel_us": round(dur_ns / 1e3, 2),
+        "gpu_cycles": cycles,
+        "sclk_ghz": round(cycles / dur_ns, 3),
+        "mfma_busy_cycles": c["SQ_VALU_MFMA_BUSY_CYCLES"],
+        # fraction of SIMD-cycles in which the matrix core was busy
+        "mfma_util": round(c["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * simds), 4),
+        "mfma_flops_issued": c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0,
+        "issued_over_algorithmic": round(c["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512.0 / alg_flops, 4)
+        if alg_flops else None,
+        "wait_inst_over_wave_cycles": round(c["SQ_WAIT_INST_ANY"] / c["SQ_WAVE_CYCLES"], 4),
+        "coexec_over_mfma_busy": round(c["SQ_VALU_MFMA_COEXEC_CYCLES"] / c["SQ_VALU_MFMA_BUSY_CYCLES"], 4),
+        "valu_insts": c["SQ_INSTS_VALU"],
+        # the bf16 MFMA peak at the clock the kernel actually ran at
+        "mfma_peak_at_sclk_tflops": round(cus * 4096.0 * cycles / dur_ns / 1e3, 1),
+    })
+    # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB) scaled by the 1 GiB copy's reading
+    try:
+        fv, _ = raw["passes"]["fetch"]
+        wv, _ = raw["passes"]["write"]
+        copy_kib = COPY_MIB * 1024.0
+
+        def copy_reading(v, counter):
+            xs = sorted(v[COPY_KERNEL][counter])
+            big = [x for x in xs if x >= 0.5 * xs[-1]]  # the calibration copies, not small transfers
+            return float(np.mean(big))
+        f_scale = copy_kib / copy_reading(fv, "FETCH_SIZE")
+        w_scale = copy_kib / copy_reading(wv, "WRITE_SIZE")
+        fk = _mean_tail(fv[k]["FETCH_SIZE"])
+        wk = _mean_tail(wv[k]["WRITE_SIZE"])
+        traffic = (fk * f_scale + wk * w_scale) * 1024.0
+        out.update({"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "fetch_scale": round(f_scale, 4),
+                    "write_scale": round(w_scale, 4), "hbm_bytes": round(traffic),
+                    "hbm_over_algorithmic": round(traffic / alg_bytes, 4) if alg_bytes else None})
+    except (KeyError, ValueError, ZeroDivisionError) as e:
+        out["traffic_error"] = repr(e)
+    return out
+
+
+def counter_child(args, fa, W, hip, dev, stream):
+    """Body of a counter pass: a 1 GiB device copy (the calibration) then a few steps."""
+    import torch
+    n = COPY_MIB << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, 0, args.dtype,
+                  args.alibi, args.seed)
+    return 0
+
+
+def counters_markdown(res, raw, workload, dtype):
+    """Markdown summary of the counter passes (for profiles/)."""
+    lines = ["# Counters of the attention kernel on workload %s (%s)" % (workload, dtype), "",
+             "Each pass is a separate `rocprofv3 --pmc` run of a short bench run (1 GiB device copy,",
+             "then 1 warm-up + 3 steps); values are per dispatch, averaged over the dispatches after",
+             "the first.  MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x",
+             "1024 SIMDs).  HBM bytes = FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for",
+             "the 1 GiB copy.", "",
+             "- kernel source sha256/16: `%s`" % kernel_sha()]
+    for key, val in res.items():
+        lines.append("- %s: `%s`" % (key, val))
+    lines += ["", "Commands (repository root):", "", "```"]
+    lines += ["rocprofv3 " + c for c in raw.get("commands", [])]
+    lines += ["```", ""]
+    return "\n".join(lines)
+
+
+# ------------------------------------------------------------------ timing
+
+def time_workload(fa, W, hip, dev, stream, name, K, warmup, every, dtype="bf16", alibi=False, seed=None):
+    """Time K calls of one workload; returns the measurements and the algorithmic work.
+
+    ``every`` = 0: no HIP events (counter passes)."""
+    import torch
+    print("bench: generating %s" % name, file=sys.stderr, flush=True)
+    wl = W.make_config(name, seed, dtype=dtype)
+    work = work_of(wl)
+    decode = name in DECODE
+    # enough input copies that consecutive steps do not hit in the 256 MB MALL
+    per_copy = (wl.k.numel() + wl.v.numel() + 2 * wl.q.numel()) * 2
+    ncopies = int(min(8, max(1, math.ceil(2.0e9 / per_copy))))
+    with torch.cuda.stream(stream):
+        copies = []
+        for _ in range(ncopies):
+            d = dict(q=wl.q.to(dev), k=wl.k.to(dev), v=wl.v.to(dev),
+                     cu_q=torch.from_numpy(wl.cu_seqlens_q).to(dev),
+                     cu_k=torch.from_numpy(wl.cu_seqlens_k).to(dev),
+                     bt=None if wl.block_table is None else torch.from_numpy(wl.block_table).to(dev))
+            d["out"] = torch.empty_like(d["q"])
+            copies.append(d)
+        torch.cuda.synchronize()
+    calls = []
+    ws_bytes = 0
+    for d in copies:
+        dq, dk, dv, do = fa._tdesc(d["q"]), fa._tdesc(d["k"]), fa._tdesc(d["v"]), fa._tdesc(d["out"])
+        dbt = fa._tdesc(d["bt"]) if d["bt"] is not None else None
+        ws_bytes = fa.fa_varlen_workspace_bytes(dq, dk, dv, wl.batch, dbt, wl.page_block_size)
+        calls.append((dq, dk, dv, do, dbt, d))
+    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    sh = stream.cuda_stream
+    alibi_t = torch.from_numpy(W.alibi_slopes(wl.num_heads)).to(dev) if alibi else None
+    dal = fa._tdesc(alibi_t) if alibi_t is not None else None
+
+    def step(i, ev_k=None):
+        dq, dk, dv, do, dbt, d = calls[i % ncopies]
+        if ev_k is not None:
+            fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
+        rc = fa.fa_varlen_fwd(dq, dk, dv, do, d["cu_q"].data_ptr(), d["cu_k"].data_ptr(), wl.batch,
+                              dbt, wl.page_block_size, wl.softmax_scale, wl.window_left,
+                              wl.window_right, 0, workspace.data_ptr() if ws_bytes else 0,
+                              ws_bytes, sh, dal)
+        if rc:
+            raise RuntimeError(fa.fa_last_error())
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    sampled = [i for i in range(K) if every and i % every == every // 2] or ([K // 2] if every else [])
+    ev_call = {i: (hip.event(), hip.event()) for i in sampled}
+    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
+    print("bench: timing %d steps of %s (events on %d of them)" % (K, name, len(sampled)),
+          file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        if i in ev_call:
+            hip.record(ev_call[i][0], sh)
+            step(i, ev_kern[i])
+            hip.record(ev_call[i][1], sh)
+            fa.fa_varlen_set_kernel_events(0, 0)
+        else:
+            step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    fa.fa_varlen_set_kernel_events(0, 0)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    call_ms = np.array([hip.elapsed_ms(*ev_call[i]) for i in sampled])
+    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
+    for a, b in list(ev_call.values()) + list(ev_kern.values()):
+        hip.destroy(a)
+        hip.destroy(b)
+    del copies, calls, workspace, alibi_t
+    torch.cuda.empty_cache()
+    return dict(wl=wl, work=work, decode=decode, ms_per_step=ms_per_step, call_ms=call_ms, kern_ms=kern_ms,
+                ncopies=ncopies, ws_bytes=ws_bytes)
+
+
+def summarize(t):
+    """Throughput and both roofline fractions of one timed workload."""
+    work, decode = t["work"], t["decode"]
+    kern = float(t["kern_ms"].mean()) if t["kern_ms"].size else float("nan")
+    call = float(t["call_ms"].mean()) if t["call_ms"].size else float("nan")
+    if decode:
+        per_step = work["kv_bytes"] / (t["ms_per_step"] * 1e-3) / 1e9
+        ach = work["total_bytes"] / (kern * 1e-3) / 1e9
+        ach_call = work["total_bytes"] / (call * 1e-3) / 1e9
+        peak, unit, bound = PEAK_HBM_GBS, "GB/s", "hbm"
+        value_unit = "GB/s"
+    else:
+        per_step = work["flops"] / (t["ms_per_step"] * 1e-3) / 1e12
+        ach = work["flops"] / (kern * 1e-3) / 1e12
+        ach_call = work["flops"] / (call * 1e-3) / 1e12
+        peak, unit, bound = PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
+        value_unit = "TFLOP/s"
+    return dict(value=round(per_step, 3), unit=value_unit, ms_per_step=round(t["ms_per_step"], 5),
+                kernel_ms_mean=round(kern, 5), call_ms_mean=round(call, 5), bound=bound,
+                achieved=round(ach, 2), achieved_call=round(ach_call, 2), peak=peak, roof_unit=unit,
+                frac=round(ach / peak, 4), frac_call=round(ach_call / peak, 4),
+                event_sampled_steps=int(t["kern_ms"].size))
+
+
+def workload_config(wl, name, alibi):
+    return {"workload": "%s: %s" % (name, wl.extra.get("desc", "")), "batch": wl.batch,
+            "total_q": int(wl.lens_q.sum()), "total_k": int(wl.lens_k.sum()), "num_heads": wl.num_heads,
+            "num_heads_k": wl.num_heads_k, "head_dim": wl.head_dim, "page_block_size": wl.page_block_size,
+            "window_left": wl.window_left, "window_right": wl.window_right, "alibi": bool(alibi),
+            "parallelism": "single GPU"}
+
+
 # ---------------------------------------------------------------------- main
+
+HEADLINE = "c4"
+SUITE = ["c2", "c3", "c5a", "c5b"]
+
 
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=None,
-                    help="c1..c5b (forward, append; default c2) or p2/p4 (padded; default p4)")
+                    help="c1..c5b: time one forward workload (default: the headline c4 plus the suite); "
+                         "append: c2..c5b (default c2); padded: p2/p4 (default p4)")
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--dtype", default="bf16", choices=["bf16", "f16"],
                     help="element type of q/k/v/out (and the append's rows and pools)")
@@ -516,7 +804,13 @@ def main(argv=None):
                     help="fwd: the attention forward (default); append: the paged K/V append; "
                          "padded: the batch-major entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--event-every", type=int, default=8, metavar="N",
+    ap.add_argument("--no-counters", action="store_true",
+                    help="skip the rocprofv3 counter passes of the default run")
+    ap.add_argument("--counters-dir", default=None,
+                    help="where the counter passes write (default gpurun_out/bench_counters if that "
+                         "folder's parent exists, else a temporary folder)")
+    ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
+    ap.add_argument("--event-every", type=int, default=4, metavar="N",
                     help="bracket the call and its main kernel with HIP events on every N-th timed "
                          "step (an event record costs ~3 us of stream time, so not on every step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -525,8 +819,9 @@ def main(argv=None):
                                                             "COPY_WRITE_CSV"),
                     help="print the HBM-traffic summary of rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
+    suite = args.op == "fwd" and args.workload is None and not args.counter_child
     if args.workload is None:
-        args.workload = "p4" if args.op == "padded" else "c2"
+        args.workload = {"padded": "p4", "append": "c2"}.get(args.op, HEADLINE)
     valid = ["p2", "p4"] if args.op == "padded" else ["c1", "c2", "c3", "c4", "c5a", "c5b"]
     if args.workload not in valid:
         ap.error("--op %s takes --workload in %s" % (args.op, valid))
@@ -538,6 +833,21 @@ def main(argv=None):
         print("bench.py: this path runs on one GPU only; --gpus %d is not supported "
               "(no multi-GPU sharding is built)" % args.gpus, file=sys.stderr, flush=True)
         return 2
+
+    # counter passes first, as child processes, before this process touches the GPU
+    raw_counters = None
+    counters_dir = None
+    if suite and not args.no_counters and os.environ.get("FA_BENCH_CHILD") != "1":
+        import tempfile
+        # import torch here (no GPU initialisation yet) so the children find it in
+        # the page cache: the first import on a fresh machine can take minutes
+        print("bench: importing torch", file=sys.stderr, flush=True)
+        import torch  # noqa: F401
+        counters_dir = args.counters_dir
+        if counters_dir is None:
+            counters_dir = (os.path.join(ROOT, "gpurun_out", "bench_counters")
+                            if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else tempfile.mkdtemp())
+        raw_counters = run_counter_passes(HEADLINE, args.dtype, counters_dir)
 
     import torch
     import varlen_flash_attention_fa_amd as fa
@@ -559,143 +869,81 @@ def main(argv=None):
 
     fa.load()
     hip = Hip()
+    if args.counter_child:
+        return counter_child(args, fa, W, hip, dev, stream)
     if args.op == "append":
         return bench_append(args, fa, W, hip, dev, stream)
     if args.op == "padded":
         return bench_padded(args, fa, W, hip, dev, stream)
-    print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
-    wl = W.make_config(args.workload, args.seed, dtype=args.dtype)
-    work = work_of(wl)
-    decode = args.workload in DECODE
 
-    # enough input copies that consecutive steps do not hit in the 256 MB MALL
-    per_copy = (wl.k.numel() + wl.v.numel() + 2 * wl.q.numel()) * 2
-    ncopies = int(min(8, max(1, math.ceil(2.0e9 / per_copy))))
-    with torch.cuda.stream(stream):
-        copies = []
-        for c in range(ncopies):
-            d = dict(q=wl.q.to(dev), k=wl.k.to(dev), v=wl.v.to(dev),
-                     cu_q=torch.from_numpy(wl.cu_seqlens_q).to(dev),
-                     cu_k=torch.from_numpy(wl.cu_seqlens_k).to(dev),
-                     bt=None if wl.block_table is None else torch.from_numpy(wl.block_table).to(dev))
-            d["out"] = torch.empty_like(d["q"])
-            copies.append(d)
-        torch.cuda.synchronize()
+    props = torch.cuda.get_device_properties(dev)
+    head = time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, args.event_every,
+                         args.dtype, args.alibi, args.seed)
+    hs = summarize(head)
+    wl, work = head["wl"], head["work"]
 
-    def descs(d):
-        dq, dk, dv, do = (fa._tdesc(d["q"]), fa._tdesc(d["k"]), fa._tdesc(d["v"]),
-                          fa._tdesc(d["out"]))
-        dbt = fa._tdesc(d["bt"]) if d["bt"] is not None else None
-        return dq, dk, dv, do, dbt
+    counters = None
+    if raw_counters is not None:
+        counters = derive_counters(raw_counters, "attn_fwd_kernel", work["flops"], work["total_bytes"],
+                                   props.multi_processor_count)
+        if counters_dir:
+            with open(os.path.join(counters_dir, "summary.md"), "w") as f:
+                f.write(counters_markdown(counters, raw_counters, args.workload, args.dtype))
+    traffic = None
+    if counters and "hbm_bytes" in counters:
+        traffic = counters["hbm_bytes"]
+    elif not suite:
+        traffic = stored_traffic(args.workload, "fwd", args.dtype, args.alibi)
+    roof = {"bound": hs["bound"], "achieved": hs["achieved"], "peak": hs["peak"], "unit": hs["roof_unit"],
+            "frac": hs["frac"], "traffic": traffic, "achieved_call": hs["achieved_call"],
+            "frac_call": hs["frac_call"],
+            "mfma_util_counters": counters.get("mfma_util") if counters else None}
 
-    calls = []
-    ws_bytes = 0
-    for d in copies:
-        dq, dk, dv, do, dbt = descs(d)
-        ws_bytes = fa.fa_varlen_workspace_bytes(dq, dk, dv, wl.batch, dbt, wl.page_block_size)
-        calls.append((dq, dk, dv, do, dbt, d))
-    workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    sh = stream.cuda_stream
-    alibi_t = torch.from_numpy(W.alibi_slopes(wl.num_heads)).to(dev) if args.alibi else None
-    dal = fa._tdesc(alibi_t) if alibi_t is not None else None
-
-    def step(i, ev_k=None):
-        dq, dk, dv, do, dbt, d = calls[i % ncopies]
-        if ev_k is not None:
-            fa.fa_varlen_set_kernel_events(ev_k[0], ev_k[1])
-        rc = fa.fa_varlen_fwd(dq, dk, dv, do, d["cu_q"].data_ptr(), d["cu_k"].data_ptr(), wl.batch,
-                              dbt, wl.page_block_size, wl.softmax_scale, wl.window_left,
-                              wl.window_right, 0, workspace.data_ptr() if ws_bytes else 0,
-                              ws_bytes, sh, dal)
-        if rc:
-            raise RuntimeError(fa.fa_last_error())
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    K = args.steps
-    every = max(1, args.event_every)
-    sampled = [i for i in range(K) if i % every == every // 2] or [K // 2]
-    ev_call = {i: (hip.event(), hip.event()) for i in sampled}
-    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
-    print("bench: timing %d steps (events on %d of them)" % (K, len(sampled)), file=sys.stderr,
-          flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        if i in ev_call:
-            hip.record(ev_call[i][0], sh)
-            step(i, ev_kern[i])
-            hip.record(ev_call[i][1], sh)
-            fa.fa_varlen_set_kernel_events(0, 0)
-        else:
-            step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    fa.fa_varlen_set_kernel_events(0, 0)
-
-    ms_per_step = (t1 - t0) * 1e3 / K
-    call_ms = np.array([hip.elapsed_ms(*ev_call[i]) for i in sampled])
-    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
-    for a, b in list(ev_call.values()) + list(ev_kern.values()):
-        hip.destroy(a)
-        hip.destroy(b)
-    kern_mean = float(kern_ms.mean())
-
-    if decode:
-        value = work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9
-        unit = "GB/s"
-        achieved = work["total_bytes"] / (kern_mean * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    else:
-        value = work["flops"] / (ms_per_step * 1e-3) / 1e12
-        unit = "TFLOP/s"
-        achieved = work["flops"] / (kern_mean * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-    traffic = stored_traffic(args.workload, "fwd", args.dtype, args.alibi)
-    roof["traffic"] = traffic
+    suite_out = {}
+    if suite:
+        for name in SUITE:
+            t = time_workload(fa, W, hip, dev, stream, name, args.steps, args.warmup, args.event_every,
+                              args.dtype, args.alibi, args.seed)
+            s = summarize(t)
+            s["config"] = workload_config(t["wl"], name, args.alibi)
+            s["algorithmic_flop"] = t["work"]["flops"]
+            s["algorithmic_total_bytes"] = t["work"]["total_bytes"]
+            s["algorithmic_kv_bytes"] = t["work"]["kv_bytes"]
+            suite_out[name] = s
+            del t
 
     cpu = None
     if not args.no_cpu_baseline:
         print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(wl, work, decode, W.alibi_slopes(wl.num_heads) if args.alibi else None)
+        cpu = cpu_baseline(wl, work, head["decode"], W.alibi_slopes(wl.num_heads) if args.alibi else None)
 
-    props = torch.cuda.get_device_properties(dev)
     line = {
         "metric": METRIC,
-        "value": round(value, 3),
-        "unit": unit,
+        "value": hs["value"],
+        "unit": hs["unit"],
         "n_gpus": 1,
-        "steps": K,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": hs["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": args.dtype,
         "data": "synthetic (seeded N(0,1) %s, seed %d)" % (args.dtype, wl.seed),
-        "config": {
-            "workload": "%s: %s" % (args.workload, wl.extra.get("desc", "")),
-            "batch": wl.batch, "total_q": int(wl.lens_q.sum()), "total_k": int(wl.lens_k.sum()),
-            "num_heads": wl.num_heads, "num_heads_k": wl.num_heads_k, "head_dim": wl.head_dim,
-            "page_block_size": wl.page_block_size, "window_left": wl.window_left,
-            "window_right": wl.window_right, "alibi": bool(args.alibi), "parallelism": "single GPU",
-        },
+        "config": workload_config(wl, args.workload, args.alibi),
         "roofline": roof,
         "cpu_baseline": cpu,
+        "suite": suite_out or None,
+        "counters": counters,
         "detail": {
-            "main_kernel_ms_mean": round(kern_mean, 5),
-            "event_sampled_steps": len(sampled),
-            "main_kernel_ms_p50": round(float(np.median(kern_ms)), 5),
-            "call_ms_p10_p50_p90": [round(float(np.percentile(call_ms, q)), 5) for q in (10, 50, 90)],
+            "main_kernel_ms_mean": hs["kernel_ms_mean"],
+            "call_ms_mean": hs["call_ms_mean"],
+            "event_sampled_steps": hs["event_sampled_steps"],
             "algorithmic_flop": work["flops"], "algorithmic_kv_bytes": work["kv_bytes"],
             "algorithmic_total_bytes": work["total_bytes"], "visible_pairs_per_head": work["pairs"],
-            "tflops_per_step": round(work["flops"] / (ms_per_step * 1e-3) / 1e12, 3),
-            "kv_gbs_per_step": round(work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9, 2),
-            "input_copies_rotated": ncopies, "workspace_bytes": ws_bytes,
+            "tflops_per_step": round(work["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 3),
+            "kv_gbs_per_step": round(work["kv_bytes"] / (head["ms_per_step"] * 1e-3) / 1e9, 2),
+            "input_copies_rotated": head["ncopies"], "workspace_bytes": head["ws_bytes"],
             "kernel_source_sha256_16": kernel_sha(), "device": props.name,
             "cus": props.multi_processor_count,
         },

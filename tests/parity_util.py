@@ -7,14 +7,34 @@ import varlen_flash_attention_fa_amd as fa
 
 MAX_ABS = 2e-2     # bf16 output vs fp64 oracle, worst element
 MEAN_ABS = 2e-3    # mean over all compared elements
-# natural-log sum-exp, fp32 vs fp64.  The kernel's row sum adds the probabilities
-# after their rounding to the 16-bit type that feeds the PV product (so out is
-# normalised by exactly the weights it used); one round-to-nearest bf16 value is
-# off by at most 2^-8 of itself, so the sum of non-negative terms is too and
-# |d lse| <= -ln(1 - 2^-8) = 3.92e-3, plus fp32 rounding of the scores.  When many
-# comparable terms share a row the errors average out; when one term dominates
-# (ALiBi's distance penalty) the bound is nearly reached.
-LSE_ABS = 4e-3
+
+
+def lse_bound(dtype, n_keys: int) -> float:
+    """Largest |lse_gpu - lse_oracle| the kernel's arithmetic allows (natural log).
+
+    No LSE tolerance is stated, so it is derived.  The kernel normalises by
+    l = sum of the probabilities p_j = 2^(s_j - m) after rounding each to the
+    16-bit type that feeds the PV product, with m placed so that the largest p is
+    in [1, 2^8], hence l >= 1.  Relative error of l, term by term:
+      * round to nearest of a normal value: u = 2^-8 (bf16) or 2^-11 (fp16);
+      * fp16 only: p below 2^-14 is subnormal and rounds with an absolute error
+        of at most 2^-25, so at most n_keys * 2^-25 relative to l >= 1 (bf16
+        shares fp32's exponent range and has no such loss);
+      * fp32 row sum: about n_keys / 32 + 16 sequential additions of 2^-24 each;
+      * fp32 exponent arguments, v_exp_f32 and v_log_f32: below 2^-20 together.
+    A relative error e of l moves lse by at most -ln(1 - e).  bf16 gives
+    3.93e-3 at 4096 keys; fp16 6.2e-4 at 4097 keys.
+    """
+    import math
+    name = str(dtype)
+    u = 2.0 ** -11 if ("float16" in name and "bfloat16" not in name) or name == "f16" else 2.0 ** -8
+    sub = n_keys * 2.0 ** -25 if u == 2.0 ** -11 else 0.0
+    e = u + sub + (n_keys / 32.0 + 16.0) * 2.0 ** -24 + 2.0 ** -20
+    return -math.log1p(-e)
+
+
+# the bf16 bound at the longest key range any test uses (70k keys): 4.06e-3
+LSE_ABS = lse_bound("bf16", 1 << 17)
 
 
 def to_dev(wl, dev="cuda"):
@@ -35,8 +55,12 @@ def run_hip(wl, dev_inputs=None, out=None, return_lse=True):
     return res
 
 
-def assert_close(out_gpu, lse_gpu, ref_out, ref_lse, rows=None, what=""):
-    """Element-wise parity against the oracle on the selected token rows."""
+def assert_close(out_gpu, lse_gpu, ref_out, ref_lse, rows=None, what="", n_keys=None):
+    """Element-wise parity against the oracle on the selected token rows.
+
+    The lse tolerance is ``lse_bound`` for the output's element type at
+    ``n_keys`` (the longest key range of the call; default 2^17)."""
+    lse_abs = lse_bound(out_gpu.dtype, n_keys if n_keys is not None else 1 << 17)
     o = out_gpu.float().cpu().double().numpy()
     l = lse_gpu.cpu().double().numpy() if lse_gpu is not None else None
     if rows is not None:
@@ -57,5 +81,6 @@ def assert_close(out_gpu, lse_gpu, ref_out, ref_lse, rows=None, what=""):
         assert np.all(l[~fin] == ref_lse[~fin]), what + ": lse of empty rows"
         if fin.any():
             le = np.abs(l[fin] - ref_lse[fin])
-            assert le.max() <= LSE_ABS, "%s: lse max|d|=%.3g mean|d|=%.3g" % (what, le.max(), le.mean())
+            assert le.max() <= lse_abs, "%s: lse max|d|=%.3g mean|d|=%.3g (bound %.3g)" % (
+                what, le.max(), le.mean(), lse_abs)
     return err

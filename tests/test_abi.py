@@ -72,7 +72,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_every_golden_text_is_in_the_library_source():
-    src = open(os.path.join(ROOT, "varlen_flash_attention_fa_amd", "csrc", "fa_api.cpp")).read()
+    # the C ABI raises the tensor texts; the offsets arrays reach it as bare
+    # pointers, so their layout texts are raised by the binding
+    pkg = os.path.join(ROOT, "varlen_flash_attention_fa_amd")
+    src = open(os.path.join(pkg, "csrc", "fa_api.cpp")).read() + open(os.path.join(pkg, "__init__.py")).read()
     for code, text, _ in golden():
         fixed = re.split(r"\{[^}]*\}", text)[0].strip()
         assert fixed in src, text
@@ -211,6 +214,30 @@ def test_dtype_heads_and_out(lib):
     rc, msg = check(desc([5, 2, 600]), desc([5, 1, 600]), desc([5, 1, 600]), batch=1)
     assert rc == 5
     assert check(Q, K3, K3, batch=-1)[0] == 7
+
+
+def test_quoted_chain_precedes_dtype_check(lib):
+    # the dtype rule is not on the pages, so every quoted check wins over it:
+    # a rank-4 int32 q reports the rank-3 text, a non-contiguous int32 k the
+    # contiguity text, a paged int32 pool of the wrong page size the page text
+    I = FA_DTYPE_I32
+    code, t, _ = tmpl("flash-attn-varlen expects input tensors of rank 3")
+    rc, msg = check(desc([2, 86, 4, 64], dtype=I), K3, K3)
+    assert rc == code and msg == render(t, q_rank="4", k_rank="3", v_rank="3")
+    rc, msg = check(Q, desc([86, 2, 64], [256, 128, 2], dtype=I), desc([86, 2, 64], dtype=I), batch=3)
+    assert msg.startswith("the last dim of k must be contiguous")
+    kp = desc([10, 32, 2, 64], dtype=I)
+    rc, msg = check(Q, kp, kp, batch=3, bt=BT, page=64)
+    assert msg.startswith("page_block_size 64 does not match k shape")
+    rc, msg = check(Q, desc([86, 2, 32], dtype=I), desc([86, 2, 32], dtype=I), batch=3)
+    assert msg.startswith("shape mismatch q")
+    # padded entry: rank, contiguity, shapes, then dtype
+    rc, msg = pcheck(q=desc([10, 4, 64], dtype=I))
+    assert rc == 1 and "rank 4" in msg
+    rc, msg = pcheck(k=desc([2, 9, 2, 64], [2048, 128, 64, 2], dtype=I), v=desc([2, 9, 2, 64], dtype=I))
+    assert msg.startswith("the last dim of k must be contiguous")
+    rc, msg = pcheck(v=desc([2, 8, 2, 64], dtype=I))
+    assert msg.startswith("shape mismatch k")
 
 
 def test_first_failing_check_wins(lib):
@@ -393,3 +420,28 @@ def test_alibi_slopes_contract(lib):
     assert fa.fa_padded_check(QP, KP4, KP4, None, ok1) == 0
     assert fa.fa_padded_check(QP, KP4, KP4, None, desc([2, 4], dtype=FA_DTYPE_F32)) == 0
     assert fa.fa_padded_check(QP, KP4, KP4, None, desc([3, 4], dtype=FA_DTYPE_F32)) == code
+
+
+# ------------------------------------------------- offsets arrays (binding)
+
+def test_seqlens_layout_texts():
+    # the binding rejects strided offsets with the pages' texts before any device
+    # work (the tensors here are on the CPU; nothing reaches the C ABI)
+    import torch
+    q = torch.zeros(4, 2, 64, dtype=torch.bfloat16)
+    k = torch.zeros(6, 1, 64, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 2, 4], dtype=torch.int32)
+    strided = torch.tensor([0, 9, 3, 9, 6, 9], dtype=torch.int32)[::2]
+    assert not strided.is_contiguous()
+    for args, text in (((strided, cu), "seqlens_q has to be contiguous"),
+                       ((cu, strided), "seqlens_k has to be contiguous")):
+        c, t, _ = tmpl(text)
+        with pytest.raises(fa.FlashAttnError) as e:
+            fa.varlen_fwd(q, k, k, *args)
+        assert e.value.code == c and str(e.value) == t
+    with pytest.raises(fa.FlashAttnError) as e:
+        fa.varlen_fwd(q, k, k, cu.long(), cu)
+    assert "int32" in str(e.value)
+    with pytest.raises(fa.FlashAttnError) as e:
+        fa.kv_append(k, k, cu, strided, torch.zeros(2, 1, dtype=torch.int32), k, k)
+    assert str(e.value) == "seqlens_k has to be contiguous"

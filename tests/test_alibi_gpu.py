@@ -1,6 +1,7 @@
 """GPU parity of the ALiBi term (alibi_slopes) through the C ABI, against the
 fp64 oracle with the same slopes: same bar as the plain forward (out max |d| <=
-2e-2, mean |d| <= 2e-3, lse within 2e-3).  Cases cover both kernel paths,
+2e-2, mean |d| <= 2e-3, lse within the bound of
+parity_util.lse_bound).  Cases cover both kernel paths,
 packed and paged K/V, windows, per-head and per-sequence slopes, forced key
 splits, scale 0, fp16, and the padded entry."""
 import numpy as np
@@ -75,7 +76,7 @@ def test_alibi_scale_zero_and_f16(oracle_mod):
     wl = W.make_custom([64, 1], [64, 300], 8, 2, 128, seed=813, page=64, dtype="f16")
     out, lse = run(wl, W.alibi_slopes(8))
     ref_o, ref_l = oracle_mod.attention_workload(wl, alibi_slopes=W.alibi_slopes(8))
-    assert_close(out, lse, ref_o, ref_l, what="alibi f16")
+    assert_close(out, lse, ref_o, ref_l, what="alibi f16", n_keys=300)
 
 
 def test_alibi_padded(oracle_mod):

@@ -1,7 +1,10 @@
 """GPU parity of the fp16 (IEEE binary16) instantiation through the C ABI.
 
-Same bar as bf16: out within max |d| <= 2e-2 and mean |d| <= 2e-3 of the fp64
-oracle on the same fp16 inputs, lse within 2e-3; the append stays bit-exact.
+Same output bar as bf16: out within max |d| <= 2e-2 and mean |d| <= 2e-3 of
+the fp64 oracle on the same fp16 inputs.  lse within the fp16 bound derived in
+parity_util.lse_bound (2^-11 rounding of the probabilities, their subnormal
+range, fp32 sums): about 6.2e-4 at 4097 keys, where bf16 allows 3.9e-3.  The
+append stays bit-exact.
 Covers configuration 1, every small shape of the bf16 suite (both kernel paths,
 head dims 13-512, paged and packed, windows), the full-size paged decode and
 long-prefill workloads on sampled rows, the padded entry and the append.
@@ -12,7 +15,7 @@ import torch
 
 import varlen_flash_attention_fa_amd as fa
 import workloads as W
-from parity_util import assert_close, run_hip
+from parity_util import assert_close, lse_bound, run_hip
 from test_parity_gpu import SMALL
 
 pytestmark = pytest.mark.gpu
@@ -34,7 +37,8 @@ def check(oracle_mod, wl, what, rows=None):
         sel = np.zeros(wl.q.shape[0], np.uint8)
         sel[rows] = 1
     ref_o, ref_l = oracle_mod.attention_workload(wl, token_sel=sel)
-    return assert_close(out, lse, ref_o, ref_l, rows=rows, what=what)
+    return assert_close(out, lse, ref_o, ref_l, rows=rows, what=what,
+                        n_keys=int(max([1] + list(wl.lens_k))))
 
 
 def test_config1_f16(oracle_mod):
@@ -77,7 +81,7 @@ def test_padded_f16(oracle_mod):
     o = out.float().cpu().double().numpy()
     err = np.abs(o - ref_o)
     assert err.max() <= 2e-2 and err.mean() <= 2e-3, (err.max(), err.mean())
-    assert np.abs(lse.cpu().double().numpy() - ref_l).max() <= 2e-3
+    assert np.abs(lse.cpu().double().numpy() - ref_l).max() <= lse_bound("f16", 170)
 
 
 def test_append_f16_bit_exact(oracle_mod):

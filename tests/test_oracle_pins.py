@@ -207,7 +207,11 @@ def test_config1_matches_torch_sdpa_fp64(oracle_mod):
 
 @pytest.mark.parametrize("Lq,Lk,wl_,wr_", [(5, 9, -1, 0), (9, 5, -1, 0), (8, 8, 2, 1),
                                           (3, 12, 4, -1), (7, 7, 0, 0), (6, 10, -1, -1),
-                                          (4, 20, 3, 2)])
+                                          (4, 20, 3, 2),
+                                          # windows at the int32 limit act as no limit,
+                                          # also on rows before the first key (Lq > Lk)
+                                          (9, 5, 2 ** 31 - 1, 0), (5, 9, -1, 2 ** 31 - 1),
+                                          (9, 5, 2 ** 31 - 1, 2 ** 31 - 1), (9, 5, 3, 2 ** 31 - 2)])
 def test_visible_set_equals_band_matrix(oracle_mod, Lq, Lk, wl_, wr_):
     # Q = 0 and V[j, d] = [j == d]: out[i, d] = 1/n_i exactly where key d is visible
     wl = W.make_custom([Lq], [Lk], 1, 1, Lk, seed=12, window_left=wl_, window_right=wr_)

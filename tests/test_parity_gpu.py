@@ -41,7 +41,8 @@ def check(oracle_mod, wl, what, rows=None):
         sel = np.zeros(wl.q.shape[0], np.uint8)
         sel[rows] = 1
     ref_o, ref_l = oracle_mod.attention_workload(wl, token_sel=sel)
-    return assert_close(out, lse, ref_o, ref_l, rows=rows, what=what)
+    return assert_close(out, lse, ref_o, ref_l, rows=rows, what=what,
+                        n_keys=int(max([1] + list(wl.lens_k))))
 
 
 # ------------------------------------------------------- configuration 1
@@ -264,11 +265,29 @@ def _sample_rows(wl, n, seed):
     return np.array(sorted(rows))
 
 
+@pytest.mark.parametrize("seed", [None, 1, 2], ids=["timing-seed", "seed1", "seed2"])
 @pytest.mark.parametrize("name,nrows", [("c2", None), ("c3", 48), ("c4", 24), ("c5a", None),
                                         ("c5b", 40)])
-def test_full_size_workloads(oracle_mod, name, nrows):
-    print("full-size %s: generating" % name, flush=True)
-    wl = W.make_config(name)
+def test_full_size_workloads(oracle_mod, name, nrows, seed):
+    # the timing seed (1001..1005) and two more draws of lengths, tables and values
+    print("full-size %s seed %s: generating" % (name, seed), flush=True)
+    wl = W.make_config(name, seed)
     rows = None if nrows is None else _sample_rows(wl, nrows, 77)
-    print("full-size %s: running" % name, flush=True)
-    check(oracle_mod, wl, name, rows=rows)
+    print("full-size %s seed %s: running" % (name, seed), flush=True)
+    check(oracle_mod, wl, "%s seed %s" % (name, seed), rows=rows)
+
+
+def test_long_prefill_window_edge_rows(oracle_mod):
+    # config 4 (window_left 4096, 8 query heads per K/V head, so a 128-row tile
+    # holds 16 queries): every row of the tiles around query 4096 of the two
+    # longest sequences, where the window's left edge enters the key range, and
+    # of the tiles at their ends, in full
+    wl = W.make_config("c4")
+    lens = wl.lens_q
+    rows = []
+    for b in np.argsort(lens)[-2:]:
+        q0, L = int(wl.cu_seqlens_q[b]), int(lens[b])
+        assert L > 4160
+        rows += list(range(q0 + 4064, q0 + 4128)) + list(range(q0 + L - 32, q0 + L))
+    print("c4 window edge: %d rows" % len(rows), flush=True)
+    check(oracle_mod, wl, "c4 window edge", rows=np.array(sorted(rows)))

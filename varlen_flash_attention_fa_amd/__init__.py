@@ -137,6 +137,22 @@ def _raise_on(rc: int) -> None:
         raise FlashAttnError(rc, fa_last_error())
 
 
+def _check_seqlens(named) -> None:
+    """Offsets arrays go to the C ABI as bare pointers, so their layout is checked here.
+
+    A strided array gets the pages' text ("seqlens_q has to be contiguous", page
+    "flash-attn-varlen expects input tensors of rank 3", Related errors); dtype and
+    rank, which the pages do not show, get their own."""
+    import torch
+    texts = {"seqlens_q": "seqlens_q has to be contiguous", "seqlens_k": "seqlens_k has to be contiguous",
+             "seqlens_new": "seqlens_new has to be contiguous"}
+    for name, t in named:
+        if t.dtype != torch.int32 or t.dim() != 1:
+            raise FlashAttnError(7, "%s must be a 1-d int32 tensor (got %s, %d-d)" % (name, t.dtype, t.dim()))
+        if not t.is_contiguous():
+            raise FlashAttnError(2, texts[name])
+
+
 def fa_varlen_check(q: FaTensor, k: FaTensor, v: FaTensor, out: Optional[FaTensor], batch: int,
                     block_table: Optional[FaTensor], page_block_size: int,
                     alibi_slopes: Optional[FaTensor] = None) -> int:
@@ -250,9 +266,7 @@ def kv_append(k_new, v_new, cu_seqlens_new, cu_seqlens_k, block_table, k_cache, 
     logical key Lk_b - Lnew_b + j.  Enqueues on torch's current stream (or ``stream``).
     """
     import torch
-    for name, t in (("cu_seqlens_new", cu_seqlens_new), ("cu_seqlens_k", cu_seqlens_k)):
-        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
-            raise FlashAttnError(7, "%s must be a contiguous 1-d int32 tensor" % name)
+    _check_seqlens((("seqlens_new", cu_seqlens_new), ("seqlens_k", cu_seqlens_k)))
     batch = cu_seqlens_new.shape[0] - 1
     if cu_seqlens_k.shape[0] != batch + 1:
         raise FlashAttnError(7, "cu_seqlens_new and cu_seqlens_k must both have batch+1 entries")
@@ -282,9 +296,7 @@ def varlen_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, block_table=None,
     import torch
     if softmax_scale is None:
         softmax_scale = 1.0 / math.sqrt(q.shape[-1])
-    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
-        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
-            raise FlashAttnError(7, "%s must be a contiguous 1-d int32 tensor" % name)
+    _check_seqlens((("seqlens_q", cu_seqlens_q), ("seqlens_k", cu_seqlens_k)))
     batch = cu_seqlens_q.shape[0] - 1
     if cu_seqlens_k.shape[0] != batch + 1:
         raise FlashAttnError(7, "cu_seqlens_q and cu_seqlens_k must both have batch+1 entries")

@@ -9,8 +9,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libfa_varlen.so")
-SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_fwd.hip"),
-           os.path.join(CSRC, "fa_append.hip")]
+SOURCES = [os.path.join(CSRC, "fa_api.cpp"), os.path.join(CSRC, "fa_plan.cpp"),
+           os.path.join(CSRC, "fa_fwd.hip"), os.path.join(CSRC, "fa_append.hip")]
 ARCH = "gfx950"
 
 

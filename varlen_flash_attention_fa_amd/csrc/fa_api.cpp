@@ -81,13 +81,9 @@ int alibi_check(const fa_tensor* al, int64_t batch, int64_t num_heads) {
 int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
                int32_t batch, const fa_tensor* bt, int32_t page_block_size, const fa_tensor* alibi) {
     if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
-    for (const fa_tensor* t : {q, k, v})
-        if (t->rank < 0 || t->rank > 4)
-            return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
-    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
-        return fail(FA_ERR_DTYPE, "flash-attn-varlen takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
-                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
 
+    // the rank checks come first and index nothing; every later check reads
+    // shape/stride entries below the rank they establish (3, or 4 for paged k/v)
     const bool paged = bt != nullptr;
     const int q_rank = q->rank, k_rank = k->rank, v_rank = v->rank;
     if (q_rank != 3 || (!paged && k_rank != 3) || (!paged && v_rank != 3))
@@ -137,6 +133,9 @@ int check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const
     }
 
     // ---- checks beyond the quoted ones
+    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(FA_ERR_DTYPE, "flash-attn-varlen takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
+                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
     if (head_size < 1 || head_size > 512)
         return fail(FA_ERR_HEAD_DIM, "flash-attn-varlen supports head sizes 1..512 (got %lld)",
                     (long long)head_size);
@@ -289,12 +288,7 @@ struct Extra {
 int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
                       const fa_tensor* alibi) {
     if (!q || !k || !v) return fail(FA_ERR_ARGUMENT, "q, k and v descriptors must not be NULL");
-    for (const fa_tensor* t : {q, k, v})
-        if (t->rank < 0 || t->rank > 4)
-            return fail(FA_ERR_RANK, "tensor rank must be in 0..4 (got %d)", (int)t->rank);
-    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
-        return fail(FA_ERR_DTYPE, "flash-attn takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
-                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
+    // rank, then last-dim contiguity, then shapes, then dtypes: the varlen entry's order
     if (q->rank != 4 || k->rank != 4 || v->rank != 4)
         return fail(FA_ERR_RANK, "flash-attn expects (batch, seqlen, heads, head_dim) tensors of rank 4 (q: %d, k: %d, v: %d)",
                     (int)q->rank, (int)k->rank, (int)v->rank);
@@ -313,6 +307,9 @@ int padded_check_impl(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v
         return fail(FA_ERR_SHAPE, "shape mismatch k %s and v %s", dims(k, false).c_str(), dims(v, false).c_str());
     if (k->shape[0] != q->shape[0] || k->shape[3] != q->shape[3])
         return fail(FA_ERR_SHAPE, "shape mismatch q %s and k %s", dims(q, false).c_str(), dims(k, false).c_str());
+    if (!is_elem16(q->dtype) || k->dtype != q->dtype || v->dtype != q->dtype)
+        return fail(FA_ERR_DTYPE, "flash-attn takes bf16 or f16 q/k/v of one dtype (dtype codes q: %d, k: %d, v: %d)",
+                    (int)q->dtype, (int)k->dtype, (int)v->dtype);
     const int64_t B = q->shape[0], Sq = q->shape[1], H = q->shape[2], D = q->shape[3];
     const int64_t Sk = k->shape[1], Hk = k->shape[2];
     if (D < 1 || D > 512)

@@ -161,7 +161,7 @@ hipError_t launch_append_meta(const AppendParams& p, hipStream_t s) {
     return launch_append<VEC, 0>(p, s);
 }
 
-hipError_t g_append_last = hipSuccess;
+thread_local hipError_t g_append_last = hipSuccess;  // per calling thread, like the error text
 
 }  // namespace
 

@@ -36,6 +36,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdlib>
 #include <cstring>
@@ -167,11 +168,15 @@ struct Range {
     int lo, hi;
 };
 
+// The window edges a - window_left and a + window_right + 1 are formed in 64
+// bits: any int32 window is legal (INT32_MAX is a common "no limit"), and with
+// a near 2^31 or below 0 (more queries than keys) the 32-bit sums would wrap.
+// The clamped results lie in [0, Lk] and fit in int again.
 __device__ __forceinline__ Range row_range(const FwdParams& p, int i, int Lq, int Lk) {
-    const int a = i + Lk - Lq;
+    const int64_t a = (int64_t)i + Lk - Lq;
     Range r;
-    r.lo = p.window_left >= 0 ? max(0, a - p.window_left) : 0;
-    r.hi = p.window_right >= 0 ? min(Lk, a + p.window_right + 1) : Lk;
+    r.lo = p.window_left >= 0 ? (int)max((int64_t)0, min((int64_t)Lk, a - p.window_left)) : 0;
+    r.hi = p.window_right >= 0 ? (int)min((int64_t)Lk, max((int64_t)0, a + p.window_right + 1)) : Lk;
     return r;
 }
 
@@ -1249,14 +1254,19 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     if (lse && lane == 0) *lse = (M + __builtin_amdgcn_logf(wsum)) * 0.6931471805599453f;
 }
 
-hipError_t g_last = hipSuccess;
+thread_local hipError_t g_last = hipSuccess;  // per calling thread, like the error text
 
 // With `slots` set, report how many workgroups of the kernel the launch would
 // use can be resident on the whole GPU at once instead of launching it.
 template <class E, int DP, int MR, int WR, int BN, int NS>
 hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s, int* slots = nullptr) {
     if (slots) {
-        static int per_cu = -1;  // per kernel instantiation; the same on every CU of this target
+        // resident workgroups per CU, one cache per kernel (with and without ALiBi:
+        // their register counts differ); the same on every CU of this target
+        // (atomics: concurrent callers may fill it; they store the same value)
+        static std::atomic<int> per_cu_of[2] = {{-1}, {-1}};
+        std::atomic<int>& cache = per_cu_of[p.alibi ? 1 : 0];
+        int per_cu = cache.load(std::memory_order_relaxed);
         if (per_cu < 0) {
             int nb = 0;
             const void* fn = p.alibi ? reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, true>)
@@ -1264,16 +1274,17 @@ hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s, int*
             hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * WR, 0);
             if (e != hipSuccess) return e;
             per_cu = nb;
+            cache.store(nb, std::memory_order_relaxed);
         }
         int dev = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e != hipSuccess) return e;
-        static int cus_of[64] = {};  // compute units per device id
-        int cus = (dev >= 0 && dev < 64) ? cus_of[dev] : 0;
+        static std::atomic<int> cus_of[64] = {};  // compute units per device id
+        int cus = (dev >= 0 && dev < 64) ? cus_of[dev].load(std::memory_order_relaxed) : 0;
         if (cus <= 0) {
             e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
             if (e != hipSuccess) return e;
-            if (dev >= 0 && dev < 64) cus_of[dev] = cus;
+            if (dev >= 0 && dev < 64) cus_of[dev].store(cus, std::memory_order_relaxed);
         }
         *slots = std::max(1, per_cu * cus);
         return hipSuccess;
@@ -1330,110 +1341,9 @@ hipError_t launch_merge(const Plan& plan, const FwdParams& p, hipStream_t s) {
     }
 }
 
-int env_int(const char* name, int dflt) {
-    const char* s = std::getenv(name);
-    if (!s || !*s) return dflt;
-    return std::atoi(s);
-}
-
-size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
-
 }  // namespace
 
 const char* last_hip_error() { return hipGetErrorString(g_last); }
-
-int make_plan(const Shapes& s, Plan* plan) {
-    Plan P;
-    std::memset(&P, 0, sizeof P);
-    P.dp = s.D <= 64 ? 64 : s.D <= 128 ? 128 : s.D <= 256 ? 256 : 512;
-    const int64_t G = s.H / s.Hk;
-    const int64_t batch = std::max<int64_t>(1, s.batch);
-    const int64_t rows_avg = (s.total_q * G + batch - 1) / batch;  // rows per (sequence, kv head)
-    int kind = rows_avg <= 64 ? KIND_DECODE : KIND_PREFILL;
-    const char* force = std::getenv("FA_FORCE_PATH");
-    if (force && std::strcmp(force, "prefill") == 0) kind = KIND_PREFILL;
-    if (force && std::strcmp(force, "decode") == 0) kind = KIND_DECODE;
-    P.kind = kind;
-    if (kind == KIND_PREFILL) {
-        P.mr = P.dp <= 256 ? 32 : 16;
-        P.wr = 4;
-        P.bn = P.dp <= 128 ? 64 : 32;
-        P.chunk = INT_MAX;
-        P.chunk_min = INT_MAX;
-        P.adapt = false;
-        P.max_chunks = 1;
-        // Only a work list too short to fill one round of resident workgroups
-        // (a few row tiles over long key ranges) has its keys cut into chunks,
-        // merged by the combine kernel: about 1536 work units in all, chunks of at
-        // least 2048 keys.  Longer lists are balanced by the planner's
-        // largest-first order alone; splitting them only adds partials and the
-        // combine (a 16-sequence chunked prefill over 8k-key caches: 0.37 ms with
-        // halves, 0.35 ms without).
-        const int64_t rows = (int64_t)P.mr * P.wr;
-        const int64_t items = ((s.total_q * G + rows - 1) / rows + s.batch) * s.Hk;
-        int64_t chunk = 0;
-        if (items < 512 && s.max_lk >= 8192)
-            chunk = std::max<int64_t>(2048, (s.max_lk * items / 1536 + P.bn - 1) / P.bn * P.bn);
-        chunk = env_int("FA_SPLIT_KEYS", (int)chunk);
-        if (chunk > 0) {
-            chunk = std::max<int64_t>(P.bn, (chunk + P.bn - 1) / P.bn * P.bn);
-            const int64_t mc = (s.max_lk + chunk - 1) / chunk;
-            if (mc > 4096) return FA_ERR_ARGUMENT;
-            if (mc > 1) {
-                P.chunk = (int)chunk;
-                P.chunk_min = (int)chunk;
-                P.max_chunks = (int)mc;
-            }
-        }
-    } else {
-        P.mr = 16;
-        P.wr = rows_avg <= 16 ? 1 : 4;
-        P.bn = 32;
-        // base chunk; the planner may resize it from half to twice (a forced size
-        // is kept)
-        const int forced = env_int("FA_SPLIT_KEYS", 0);
-        int chunk = forced > 0 ? forced : 1024;
-        if (chunk < P.bn) chunk = P.bn;
-        chunk = (chunk + P.bn - 1) / P.bn * P.bn;
-        P.chunk = chunk;
-        P.adapt = forced <= 0;
-        P.chunk_min = P.adapt ? std::max(P.bn, (chunk / 2 + P.bn - 1) / P.bn * P.bn) : chunk;
-        const int64_t mc = std::max<int64_t>(1, (s.max_lk + P.chunk_min - 1) / P.chunk_min);
-        if (mc > 4096) return FA_ERR_ARGUMENT;
-        P.max_chunks = (int)mc;
-        if (P.max_chunks == 1) {
-            P.chunk = P.chunk_min = INT_MAX;
-            P.adapt = false;
-        }
-    }
-    P.rows = P.mr * P.wr;
-    const int64_t tiles = (s.total_q * G + P.rows - 1) / P.rows + s.batch;
-    const int64_t items = tiles * P.max_chunks;
-    if (items >= INT32_MAX / 2 || s.Hk > 65535) return FA_ERR_ARGUMENT;
-    // runs of units per XCD: whole heads when Hk is a multiple of 8, else runs of
-    // 8 units (neighbouring items of one head for Hk = 1)
-    P.xcd_chunk = (s.Hk % 8 == 0) ? 1 : 8;
-    if ((items * s.Hk + 64) * 8 >= (int64_t)UINT32_MAX / 2) return FA_ERR_ARGUMENT;
-    P.items_bound = items;
-    // workspace: [split partials o][split partials lse][items][count][seq offsets]
-    size_t off = 0;
-    if (P.max_chunks > 1) {
-        off += (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * (size_t)P.dp * 4u;
-        off += (size_t)P.max_chunks * (size_t)s.total_q * (size_t)s.H * 4u;
-    }
-    off = align256(off);
-    P.off_items = off;
-    off = align256(off + (size_t)items * 32u);
-    P.off_count = off;
-    off = align256(off + 4u);
-    P.off_seq = off;
-    off = align256(off + (size_t)(s.batch + 1) * 4u);
-    P.off_tok = off;
-    if (P.max_chunks > 1) off = align256(off + (size_t)s.total_q * 4u);
-    P.ws_bytes = off;
-    *plan = P;
-    return 0;
-}
 
 int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);

@@ -2,6 +2,7 @@
 // (fa_fwd.hip).  Not installed; the public ABI is include/fa_varlen.h.
 #pragma once
 
+#include <hip/hip_runtime.h>  // int4 and the runtime types; host-only users build it with -D__HIP_PLATFORM_AMD__
 #include <stddef.h>
 #include <stdint.h>
 
