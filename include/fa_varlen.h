@@ -30,8 +30,9 @@
  *
  * Ownership: the caller owns every buffer (inputs, out, softmax_lse,
  * workspace) and the stream.  The library allocates and frees nothing, keeps
- * no state between calls other than the thread-local error text, and never
- * synchronizes the device: fa_varlen_fwd only enqueues kernels on `stream`.
+ * no state between calls other than the thread-local error text (and the
+ * fixed scratch array of fa_varlen_fwd_static, part of its code object), and
+ * never synchronizes the device: fa_varlen_fwd only enqueues kernels on `stream`.
  *
  * Errors: every function returns FA_OK (0) or one of the FA_ERR_* codes; the
  * text of the last error on the calling thread is returned by fa_last_error().
@@ -130,7 +131,9 @@ int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_t
  *   window_left, window_right  query row i of a sequence sits at key position
  *       a = i + Lk - Lq; key j is visible iff j >= a - window_left (when
  *       window_left >= 0) and j <= a + window_right (when window_right >= 0).
- *       Negative = unbounded; causal is (-1, 0).  Query head h reads key/value
+ *       Negative = unbounded; causal is (-1, 0).  Any int32 value is legal: a
+ *       window at least as long as every distance (INT32_MAX, say) sees every
+ *       key on its side, as a negative one does.  Query head h reads key/value
  *       head h / (num_heads / num_heads_k).  A row that sees no key gets out = 0.
  *   alibi_slopes  NULL, or device fp32 slopes as for fa_varlen_check: the scaled
  *       score of key j for query row i of head h gets -slope * |a - j| added
@@ -147,6 +150,35 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
                   int32_t page_block_size, float softmax_scale, int32_t window_left,
                   int32_t window_right, const fa_tensor* alibi_slopes, float* softmax_lse,
                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * fa_varlen_fwd_static -- fa_varlen_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation.  Same arguments, results, checks and errors as
+ * fa_varlen_fwd, without the workspace: the scratch comes from a fixed
+ * FA_STATIC_SCRATCH_BYTES array that the library's code object holds on each
+ * GPU it runs on (from the first load of the library until the process ends).
+ * The call allocates and frees nothing.
+ *
+ *   Limit: a call whose fa_varlen_workspace_bytes() exceeds
+ *       FA_STATIC_SCRATCH_BYTES is rejected with FA_ERR_WORKSPACE (nothing is
+ *       launched); use fa_varlen_fwd with a workspace for it.
+ *   stream: must belong to the calling thread's current device (else
+ *       FA_ERR_DEVICE), whose copy of the scratch is used.
+ *   Sharing: every call on one GPU uses that GPU's one scratch, which keeps the
+ *       last call's contents (no call relies on them: all of it is written
+ *       before it is read).  Calls whose kernels can overlap on one GPU (other
+ *       streams, other threads) race on it; serialize them, for instance on one
+ *       stream.
+ */
+#define FA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+int fa_varlen_fwd_static(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v,
+                         const fa_tensor* out, const int32_t* cu_seqlens_q,
+                         const int32_t* cu_seqlens_k, int32_t batch, const fa_tensor* block_table,
+                         int32_t page_block_size, float softmax_scale, int32_t window_left,
+                         int32_t window_right, const fa_tensor* alibi_slopes, float* softmax_lse,
+                         void* stream);
 
 /*
  * Padded (non-varlen) entry: the same forward over batch-major tensors in which

@@ -148,6 +148,12 @@ int main() {
                                           INT_MAX, INT_MAX, nullptr, nullptr, nullptr, 0, nullptr), FA_ERR_DEVICE);
     expect("fwd no out", fa_varlen_fwd(&qh, &kh, &kh, nullptr, cu.data(), cu.data(), 3, nullptr, 0, 0.125f, -1, 0,
                                        nullptr, nullptr, nullptr, 0, nullptr), FA_ERR_ARGUMENT);
+    expect("static batch 0", fa_varlen_fwd_static(&qh, &kh, &kh, &oh, nullptr, nullptr, 0, nullptr, 0, 0.125f, -1,
+                                                  0, nullptr, nullptr, nullptr), FA_OK);
+    expect("static host ptrs", fa_varlen_fwd_static(&qh, &kh, &kh, &oh, cu.data(), cu.data(), 3, nullptr, 0, 0.125f,
+                                                    -1, 0, nullptr, nullptr, nullptr), FA_ERR_DEVICE);
+    expect("static contract", fa_varlen_fwd_static(&q4, &kh, &kh, &oh, cu.data(), cu.data(), 3, nullptr, 0, 0.125f,
+                                                   -1, 0, nullptr, nullptr, nullptr), FA_ERR_RANK);
     fa_tensor QP0 = T({0, 5, 4, 64}), KP0 = T({0, 9, 2, 64});
     expect("padded empty", fa_padded_fwd(&QP0, &KP0, &KP0, &QP0, 0.1f, -1, 0, nullptr, nullptr, nullptr, 0,
                                          nullptr), FA_OK);

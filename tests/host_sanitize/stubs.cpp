@@ -18,5 +18,9 @@ int launch_kv_append(const AppendParams&, void*, void*, void*) {
     std::abort();
 }
 const char* last_append_error() { return "host-only build"; }
+int static_scratch(void*, void**, size_t*) {
+    std::fprintf(stderr, "static_scratch reached in the host-only build\n");
+    std::abort();
+}
 
 }  // namespace fa

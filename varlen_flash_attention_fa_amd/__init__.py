@@ -21,7 +21,7 @@ from typing import Optional, Sequence, Tuple
 __all__ = [
     "FaTensor", "FlashAttnError", "lib_path", "load", "fa_varlen_check",
     "fa_varlen_workspace_bytes", "fa_varlen_fwd", "fa_last_error", "varlen_fwd", "desc",
-    "fa_varlen_set_kernel_events", "fa_kv_append_check", "fa_kv_append", "kv_append",
+    "fa_varlen_set_kernel_events", "fa_varlen_fwd_static", "FA_STATIC_SCRATCH_BYTES", "fa_kv_append_check", "fa_kv_append", "kv_append",
     "fa_padded_check", "fa_padded_workspace_bytes", "fa_padded_fwd", "padded_fwd",
     "FA_DTYPE_BF16", "FA_DTYPE_I32", "FA_DTYPE_F16", "FA_DTYPE_F32", "STATUS",
 ]
@@ -78,6 +78,10 @@ def load():
                                   ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, P,
                                   ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
     lib.fa_varlen_fwd.restype = ctypes.c_int
+    lib.fa_varlen_fwd_static.argtypes = [P, P, P, P, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, P,
+                                         ctypes.c_int32, ctypes.c_float, ctypes.c_int32, ctypes.c_int32, P,
+                                         ctypes.c_void_p, ctypes.c_void_p]
+    lib.fa_varlen_fwd_static.restype = ctypes.c_int
     lib.fa_varlen_set_kernel_events.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     lib.fa_varlen_set_kernel_events.restype = ctypes.c_int
     lib.fa_padded_check.argtypes = [P, P, P, P, P]
@@ -181,6 +185,22 @@ def fa_varlen_fwd(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqle
                                 int(page_block_size or 0), float(softmax_scale), int(window_left),
                                 int(window_right), _ref(alibi_slopes), softmax_lse or None,
                                 workspace or None, int(workspace_bytes), stream or None)
+
+
+# size of the scratch array fa_varlen_fwd_static uses on each GPU (FA_STATIC_SCRATCH_BYTES)
+FA_STATIC_SCRATCH_BYTES = 64 << 20
+
+
+def fa_varlen_fwd_static(q: FaTensor, k: FaTensor, v: FaTensor, out: FaTensor, cu_seqlens_q: int,
+                         cu_seqlens_k: int, batch: int, block_table: Optional[FaTensor],
+                         page_block_size: int, softmax_scale: float, window_left: int, window_right: int,
+                         softmax_lse: int, stream: int, alibi_slopes: Optional[FaTensor] = None) -> int:
+    """Raw C-ABI call of the allocation-free entry (no workspace).  Returns the status."""
+    return load().fa_varlen_fwd_static(_ref(q), _ref(k), _ref(v), _ref(out), cu_seqlens_q or None,
+                                       cu_seqlens_k or None, int(batch), _ref(block_table),
+                                       int(page_block_size or 0), float(softmax_scale), int(window_left),
+                                       int(window_right), _ref(alibi_slopes), softmax_lse or None,
+                                       stream or None)
 
 
 def fa_varlen_set_kernel_events(start_event: int, stop_event: int) -> int:

@@ -281,6 +281,7 @@ struct Extra {
     int64_t q_bx = 0, k_bx = 0, v_bx = 0, o_bx = 0;
     int64_t lse_sh = 0, lse_bx = 0;
     bool vec_ok = true;   // alignment of the strides the 3-d views do not show
+    bool static_ws = false;  // the workspace is the library's own device array
     fa::Shapes shapes{};
 };
 
@@ -380,7 +381,7 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
             return fail(FA_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", plan.ws_bytes,
                         workspace ? workspace_bytes : (size_t)0);
         if (!aligned16(workspace)) return fail(FA_ERR_WORKSPACE, "workspace must be 16-byte aligned");
-        if (!is_device_ptr(workspace)) return fail(FA_ERR_DEVICE, "workspace must be a cuda tensor");
+        if (!ex.static_ws && !is_device_ptr(workspace)) return fail(FA_ERR_DEVICE, "workspace must be a cuda tensor");
     }
 
     fa::FwdParams p;
@@ -509,6 +510,40 @@ int fa_varlen_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, co
     ex.shapes = shapes_of(q, k, batch, block_table, page_block_size);
     return run_fwd(q, k, v, out, cu_seqlens_q, cu_seqlens_k, batch, block_table, page_block_size, softmax_scale,
                    window_left, window_right, alibi_slopes, softmax_lse, workspace, workspace_bytes, stream, ex);
+}
+
+int fa_varlen_fwd_static(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,
+                         const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t batch,
+                         const fa_tensor* block_table, int32_t page_block_size, float softmax_scale,
+                         int32_t window_left, int32_t window_right, const fa_tensor* alibi_slopes,
+                         float* softmax_lse, void* stream) {
+    if (!out) return fail(FA_ERR_ARGUMENT, "out descriptor must not be NULL");
+    int rc = check_impl(q, k, v, out, batch, block_table, page_block_size, alibi_slopes);
+    if (rc) return rc;
+    if (batch == 0 || q->shape[0] == 0) return FA_OK;  // nothing to compute, nothing written
+    if (!cu_seqlens_q || !is_device_ptr(cu_seqlens_q))
+        return fail(FA_ERR_DEVICE, "seqlens_q must be a cuda tensor");
+    if (!cu_seqlens_k || !is_device_ptr(cu_seqlens_k))
+        return fail(FA_ERR_DEVICE, "seqlens_k must be a cuda tensor");
+    Extra ex;
+    ex.lse_sh = q->shape[0];
+    ex.shapes = shapes_of(q, k, batch, block_table, page_block_size);
+    ex.static_ws = true;
+    fa::Plan plan;
+    rc = fa::make_plan(ex.shapes, &plan);
+    if (rc) return fail(rc, "no launch plan for these shapes");
+    if (plan.ws_bytes > FA_STATIC_SCRATCH_BYTES)
+        return fail(FA_ERR_WORKSPACE,
+                    "fa_varlen_fwd_static: these shapes need %zu bytes of scratch, more than the %zu of the "
+                    "static scratch; call fa_varlen_fwd with a workspace instead",
+                    plan.ws_bytes, (size_t)FA_STATIC_SCRATCH_BYTES);
+    void* ws = nullptr;
+    size_t ws_bytes = 0;
+    rc = fa::static_scratch(stream, &ws, &ws_bytes);
+    if (rc == FA_ERR_DEVICE) return fail(rc, "the stream does not belong to the current device");
+    if (rc) return fail(rc, "static scratch lookup failed: %s", fa::last_hip_error());
+    return run_fwd(q, k, v, out, cu_seqlens_q, cu_seqlens_k, batch, block_table, page_block_size, softmax_scale,
+                   window_left, window_right, alibi_slopes, softmax_lse, ws, ws_bytes, stream, ex);
 }
 
 int fa_padded_check(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa_tensor* out,

@@ -40,6 +40,7 @@
 #include <climits>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/fa_varlen.h"
 #include "fa_internal.h"
@@ -1344,6 +1345,62 @@ hipError_t launch_merge(const Plan& plan, const FwdParams& p, hipStream_t s) {
 }  // namespace
 
 const char* last_hip_error() { return hipGetErrorString(g_last); }
+
+// ---------------------------------------------------------- static scratch
+//
+// Scratch of the allocation-free entry (fa_varlen_fwd_static): one array per
+// GPU in the library's code object, so a call that uses it allocates nothing.
+// In host code the name `scratch` is a host-side stand-in, not a device
+// address; the device address of each GPU's copy is looked up once, with that
+// GPU current, by hipGetSymbolAddress, and only that address ever reaches a
+// kernel.  Nothing in it has to start at zero: the planner writes the work
+// list, its count, the offsets and the per-token chunk counts before any
+// kernel reads them, and every split item writes its partials (rows without a
+// visible key included) before the combine reads them.
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[FA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+}  // namespace
+
+int static_scratch(void* stream, void** ptr, size_t* bytes) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        g_last = e;
+        return FA_ERR_HIP;
+    }
+    if (stream) {
+        hipDevice_t sdev = -1;
+        e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+        if (e != hipSuccess) {
+            g_last = e;
+            return FA_ERR_HIP;
+        }
+        if (sdev != dev) return FA_ERR_DEVICE;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return FA_ERR_DEVICE;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !p) {
+                g_last = e != hipSuccess ? e : hipErrorInvalidSymbol;
+                return FA_ERR_HIP;
+            }
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *ptr = p;
+    *bytes = (size_t)FA_STATIC_SCRATCH_BYTES;
+    return 0;
+}
 
 int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_start, void* ev_stop) {
     hipStream_t s = static_cast<hipStream_t>(stream);

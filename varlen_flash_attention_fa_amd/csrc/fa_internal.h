@@ -107,6 +107,13 @@ struct AppendParams {
 };
 
 int make_plan(const Shapes& s, Plan* plan);   // 0 or an fa_status code
+
+// Device scratch of the allocation-free entry: FA_STATIC_SCRATCH_BYTES per GPU,
+// a __device__ array of the library's code object.  Writes the calling
+// thread's current device's copy of it to *ptr (its size to *bytes); the
+// stream, when given, must belong to that device.  0, FA_ERR_DEVICE or
+// FA_ERR_HIP.
+int static_scratch(void* stream, void** ptr, size_t* bytes);
 // 0 or FA_ERR_HIP.  ev_start/ev_stop (hipEvent_t or null) bracket the main kernel.
 int launch_fwd(const Plan& plan, const FwdParams& p, void* stream, void* ev_start, void* ev_stop);
 const char* last_hip_error();
