@@ -157,10 +157,11 @@ def stored_traffic(workload: str, op: str = "fwd", dtype: str = "bf16", alibi: b
         return None
     if op == "append":
         path = os.path.join(ROOT, "profiles", "kv_append_%s_hbm_traffic.md" % workload)
-        src = APPEND_SRC
+        src, key = APPEND_SRC, "HBM bytes per launch (scaled)"
     else:
-        path = os.path.join(ROOT, "profiles", "attn_fwd_%s_hbm_traffic.md" % workload)
-        src = KERNEL_SRC
+        # the counter summary that `bench.py --workload W --counters` writes
+        path = os.path.join(ROOT, "profiles", "attn_fwd_%s_counters.md" % workload)
+        src, key = KERNEL_SRC, "hbm_bytes"
     if not os.path.exists(path):
         return None
     vals = {}
@@ -171,7 +172,7 @@ def stored_traffic(workload: str, op: str = "fwd", dtype: str = "bf16", alibi: b
     if vals.get("kernel source sha256/16") != kernel_sha(src):
         return None
     try:
-        return float(vals["HBM bytes per launch (scaled)"])
+        return float(vals[key])
     except (KeyError, ValueError):
         return None
 
@@ -567,7 +568,9 @@ def run_counter_passes(workload, dtype, outroot, timeout_s=170):
             "--output-format", "csv", "-d", d, "-o", "run", "--", sys.executable,
             os.path.join(ROOT, "bench.py"), "--counter-child", "--workload", workload, "--dtype", dtype,
             "--steps", "3", "--warmup", "1"]
-        res["commands"].append(" ".join(cmd[4:]))
+        res["commands"].append(" ".join(["rocprofv3", "--pmc"] + counters + [
+            "--output-format", "csv", "-d", os.path.relpath(d, ROOT), "-o", "run", "--", "python3", "bench.py",
+            "--counter-child", "--workload", workload, "--dtype", dtype, "--steps", "3", "--warmup", "1"]))
         print("bench: counter pass %s (%s)" % (name, " ".join(counters)), file=sys.stderr, flush=True)
         env = dict(os.environ, FA_BENCH_CHILD="1")
         import subprocess
@@ -652,8 +655,9 @@ def counter_child(args, fa, W, hip, dev, stream):
     return 0
 
 
-def counters_markdown(res, raw, workload, dtype):
-    """Markdown summary of the counter passes (for profiles/)."""
+def counters_markdown(res, raw, workload, dtype, invocation):
+    """Markdown summary of the counter passes (for profiles/); ``invocation`` is
+    the bench command that ran them."""
     lines = ["# Counters of the attention kernel on workload %s (%s)" % (workload, dtype), "",
              "Each pass is a separate `rocprofv3 --pmc` run of a short bench run (1 GiB device copy,",
              "then 1 warm-up + 3 steps); values are per dispatch, averaged over the dispatches after",
@@ -663,8 +667,9 @@ def counters_markdown(res, raw, workload, dtype):
              "- kernel source sha256/16: `%s`" % kernel_sha()]
     for key, val in res.items():
         lines.append("- %s: `%s`" % (key, val))
-    lines += ["", "Commands (repository root):", "", "```"]
-    lines += ["rocprofv3 " + c for c in raw.get("commands", [])]
+    lines += ["", "Made from the repository root by", "", "```", invocation, "```", "",
+              "which runs each counter pass as a child process:", "", "```"]
+    lines += list(raw.get("commands", []))
     lines += ["```", ""]
     return "\n".join(lines)
 
@@ -806,6 +811,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-counters", action="store_true",
                     help="skip the rocprofv3 counter passes of the default run")
+    ap.add_argument("--counters", action="store_true",
+                    help="run the counter passes for --workload too (the default run always does, "
+                         "for the headline workload)")
     ap.add_argument("--counters-dir", default=None,
                     help="where the counter passes write (default gpurun_out/bench_counters if that "
                          "folder's parent exists, else a temporary folder)")
@@ -819,7 +827,8 @@ def main(argv=None):
                                                             "COPY_WRITE_CSV"),
                     help="print the HBM-traffic summary of rocprofv3 --pmc runs and exit")
     args = ap.parse_args(argv)
-    suite = args.op == "fwd" and args.workload is None and not args.counter_child
+    suite = (args.op == "fwd" and args.workload is None and not args.counter_child
+             and not args.copy_calibration and not args.counters_summary)
     if args.workload is None:
         args.workload = {"padded": "p4", "append": "c2"}.get(args.op, HEADLINE)
     valid = ["p2", "p4"] if args.op == "padded" else ["c1", "c2", "c3", "c4", "c5a", "c5b"]
@@ -837,7 +846,14 @@ def main(argv=None):
     # counter passes first, as child processes, before this process touches the GPU
     raw_counters = None
     counters_dir = None
-    if suite and not args.no_counters and os.environ.get("FA_BENCH_CHILD") != "1":
+    # never nested: a process that already runs under rocprofv3 has its GPU
+    # initialised by the profiler's library, and its children must not exec
+    under_profiler = any(k.startswith("ROCPROF_") for k in os.environ)
+    want_counters = (suite or args.counters) and args.op == "fwd" and not args.no_counters
+    if want_counters and under_profiler:
+        print("bench: running under rocprofv3, counter passes skipped", file=sys.stderr, flush=True)
+    if (want_counters and not under_profiler and not args.counter_child and not args.copy_calibration
+            and os.environ.get("FA_BENCH_CHILD") != "1"):
         import tempfile
         # import torch here (no GPU initialisation yet) so the children find it in
         # the page cache: the first import on a fresh machine can take minutes
@@ -847,7 +863,7 @@ def main(argv=None):
         if counters_dir is None:
             counters_dir = (os.path.join(ROOT, "gpurun_out", "bench_counters")
                             if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else tempfile.mkdtemp())
-        raw_counters = run_counter_passes(HEADLINE, args.dtype, counters_dir)
+        raw_counters = run_counter_passes(args.workload, args.dtype, counters_dir)
 
     import torch
     import varlen_flash_attention_fa_amd as fa
@@ -888,7 +904,9 @@ def main(argv=None):
                                    props.multi_processor_count)
         if counters_dir:
             with open(os.path.join(counters_dir, "summary.md"), "w") as f:
-                f.write(counters_markdown(counters, raw_counters, args.workload, args.dtype))
+                f.write(counters_markdown(counters, raw_counters, args.workload, args.dtype,
+                                          " ".join(["python3", "bench.py"] + list(sys.argv[1:] if argv is None
+                                                                                  else argv))))
     traffic = None
     if counters and "hbm_bytes" in counters:
         traffic = counters["hbm_bytes"]
