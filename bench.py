@@ -15,14 +15,17 @@ U[1024,32768], page 128, D 256 MHA and D 512 MQA) as KV GB/s against HBM, and
 paged chunked prefill (16 seqs, q U[1,512] over prefixes U[0,8192], page 64)
 as TFLOP/s.  ``--workload cN`` times one workload alone.
 
-Timed region: W untimed warm-up steps, then exactly K steps bracketed by
-``torch.cuda.synchronize()``.  Consecutive steps read different copies of the
-inputs (enough copies to exceed the 256 MB last-level cache), so K/V really
-come from HBM.  Each entry reports two roofline fractions: ``frac`` for the
-attention kernel alone (its duration from HIP events that the library records
-around it on its launch stream, ``fa_varlen_set_kernel_events``, on every N-th
-timed step) and ``frac_call`` for the whole call (events around everything
-the call launches).
+Timed region: W untimed warm-up steps (continued, untimed, until at least 0.2 s
+of them have run, so the shader clock has settled), then exactly K steps bracketed by
+``torch.cuda.synchronize()``, with no per-step events (``value``, ``ms_per_step``).
+Consecutive steps read different copies of the inputs (enough copies to exceed
+the 256 MB last-level cache), so K/V really come from HBM.  A second pass of K
+steps records HIP events around the attention kernel of every call on its
+launch stream (``fa_varlen_set_kernel_events``); an event between two
+dependent kernels holds the stream for about 5 us, which is why the step time
+is taken without them.  Each entry reports two roofline fractions: ``frac``
+for the attention kernel alone (its mean event-timed duration) and
+``frac_call`` for the whole call (the step time: planner, attention, combine).
 
 Counters (default run; ``--no-counters`` skips them): before it touches the
 GPU, the bench runs itself three times under ``rocprofv3 --pmc`` (a short run
@@ -344,15 +347,13 @@ def bench_append(args, fa, W, hip, dev, stream):
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm = warm_up(step, args.warmup)
     # A step is this one kernel: two events around the whole timed region give its
     # mean duration without the per-call event cost (a few us, comparable to the
-    # kernel on the small appends).  Sampled per-call events are kept as detail.
+    # kernel on the small appends).  Per-call events, in a second pass of K steps,
+    # are kept as detail.
     K = args.steps
-    every = max(1, args.event_every)
-    sampled = [i for i in range(K) if i % every == every // 2] or [K // 2]
+    sampled = list(range(K))
     region_k = (hip.event(), hip.event())
     print("bench: timing %d append steps" % K, file=sys.stderr, flush=True)
     torch.cuda.synchronize()
@@ -403,7 +404,8 @@ def bench_append(args, fa, W, hip, dev, stream):
         "detail": {
             "append_kernel_ms_mean": round(kern_mean, 6),
             "append_kernel_ms_per_call_events_p50": round(float(np.median(kern_ms)), 6),
-            "per_call_event_samples": len(sampled), "algorithmic_total_bytes": work["total_bytes"],
+            "per_call_event_samples": len(sampled), "warmup_steps_run": warm,
+            "algorithmic_total_bytes": work["total_bytes"],
             "new_row_copies_rotated": n_new, "kernel_source_sha256_16": kernel_sha(APPEND_SRC),
             "device": props.name,
         },
@@ -456,29 +458,10 @@ def bench_padded(args, fa, W, hip, dev, stream):
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
+    warm = warm_up(step, args.warmup)
     K = args.steps
-    every = max(1, args.event_every)
-    sampled = [i for i in range(K) if i % every == every // 2] or [K // 2]
-    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
-    print("bench: timing %d padded steps (events on %d of them)" % (K, len(sampled)), file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        if i in ev_kern:
-            step(i, ev_kern[i])
-            fa.fa_varlen_set_kernel_events(0, 0)
-        else:
-            step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / K
-    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
-    for a, b in ev_kern.values():
-        hip.destroy(a)
-        hip.destroy(b)
+    ms_per_step, kern_ms = timed_passes(step, K, hip, True, "padded " + args.workload,
+                                        lambda: fa.fa_varlen_set_kernel_events(0, 0))
     kern_mean = float(kern_ms.mean())
     if decode:
         value, unit = work["kv_bytes"] / (ms_per_step * 1e-3) / 1e9, "GB/s"
@@ -508,7 +491,8 @@ def bench_padded(args, fa, W, hip, dev, stream):
                    "alibi": bool(args.alibi), "parallelism": "single GPU"},
         "roofline": roof,
         "cpu_baseline": cpu,
-        "detail": {"main_kernel_ms_mean": round(kern_mean, 5), "event_sampled_steps": len(sampled),
+        "detail": {"main_kernel_ms_mean": round(kern_mean, 5), "kernel_event_steps": int(kern_ms.size),
+                   "warmup_steps_run": warm,
                    "algorithmic_flop": work["flops"], "algorithmic_total_bytes": work["total_bytes"],
                    "input_copies_rotated": ncopies, "workspace_bytes": ws_bytes,
                    "kernel_source_sha256_16": kernel_sha(), "device": props.name},
@@ -650,7 +634,7 @@ def counter_child(args, fa, W, hip, dev, stream):
         dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
-    time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, 0, args.dtype,
+    time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, False, args.dtype,
                   args.alibi, args.seed)
     return 0
 
@@ -676,10 +660,66 @@ def counters_markdown(res, raw, workload, dtype, invocation):
 
 # ------------------------------------------------------------------ timing
 
-def time_workload(fa, W, hip, dev, stream, name, K, warmup, every, dtype="bf16", alibi=False, seed=None):
+WARMUP_MIN_S = 0.2
+
+
+def warm_up(step, W, min_s=WARMUP_MIN_S):
+    """W untimed steps, continued until at least ``min_s`` seconds of them have
+    run (synchronised), so the shader clock has left its idle level before the
+    timed steps: after 5 steps (2 ms) of the chunked-prefill call its steps took
+    0.36 ms, after 300 steps 0.30 ms.  Returns the number of steps run."""
+    import torch
+    n = 0
+    t0 = time.perf_counter()
+    while n < W or time.perf_counter() - t0 < min_s:
+        for _ in range(max(1, W if n < W else 16)):
+            step(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
+def timed_passes(step, K, hip, events, name, reset):
+    """The two timed passes of K calls each.
+
+    The first gives the step time: K calls back to back, no per-call events,
+    bracketed by device synchronisation and read on the host clock.  The second
+    repeats the K calls with the library's HIP events around the main kernel of
+    every call, on its stream, for the kernel's mean duration.  An event between
+    two dependent kernels holds the stream for about 5 us, so events in the
+    first pass would slow the short decode steps by several percent.
+    ``events`` False: the second pass is skipped (counter passes).  ``reset``
+    detaches the events from the library afterwards."""
+    import torch
+    print("bench: timing %d steps of %s" % (K, name), file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / K
+    if not events:
+        return ms_per_step, np.zeros(0)
+    ev = [(hip.event(), hip.event()) for _ in range(K)]
+    print("bench: %d more steps of %s with kernel events" % (K, name), file=sys.stderr, flush=True)
+    try:
+        for i in range(K):
+            step(i, ev[i])
+    finally:
+        reset()
+    torch.cuda.synchronize()
+    kern_ms = np.array([hip.elapsed_ms(a, b) for a, b in ev])
+    for a, b in ev:
+        hip.destroy(a)
+        hip.destroy(b)
+    return ms_per_step, kern_ms
+
+
+def time_workload(fa, W, hip, dev, stream, name, K, warmup, events, dtype="bf16", alibi=False, seed=None):
     """Time K calls of one workload; returns the measurements and the algorithmic work.
 
-    ``every`` = 0: no HIP events (counter passes)."""
+    ``events`` False: no HIP events (counter passes)."""
     import torch
     print("bench: generating %s" % name, file=sys.stderr, flush=True)
     wl = W.make_config(name, seed, dtype=dtype)
@@ -721,44 +761,19 @@ def time_workload(fa, W, hip, dev, stream, name, K, warmup, every, dtype="bf16",
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    sampled = [i for i in range(K) if every and i % every == every // 2] or ([K // 2] if every else [])
-    ev_call = {i: (hip.event(), hip.event()) for i in sampled}
-    ev_kern = {i: (hip.event(), hip.event()) for i in sampled}
-    print("bench: timing %d steps of %s (events on %d of them)" % (K, name, len(sampled)),
-          file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K):
-        if i in ev_call:
-            hip.record(ev_call[i][0], sh)
-            step(i, ev_kern[i])
-            hip.record(ev_call[i][1], sh)
-            fa.fa_varlen_set_kernel_events(0, 0)
-        else:
-            step(i)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    fa.fa_varlen_set_kernel_events(0, 0)
-    ms_per_step = (t1 - t0) * 1e3 / K
-    call_ms = np.array([hip.elapsed_ms(*ev_call[i]) for i in sampled])
-    kern_ms = np.array([hip.elapsed_ms(*ev_kern[i]) for i in sampled])
-    for a, b in list(ev_call.values()) + list(ev_kern.values()):
-        hip.destroy(a)
-        hip.destroy(b)
+    warm = warm_up(step, warmup, WARMUP_MIN_S if events else 0.0)
+    ms_per_step, kern_ms = timed_passes(step, K, hip, events, name, lambda: fa.fa_varlen_set_kernel_events(0, 0))
     del copies, calls, workspace, alibi_t
     torch.cuda.empty_cache()
-    return dict(wl=wl, work=work, decode=decode, ms_per_step=ms_per_step, call_ms=call_ms, kern_ms=kern_ms,
-                ncopies=ncopies, ws_bytes=ws_bytes)
+    return dict(wl=wl, work=work, decode=decode, ms_per_step=ms_per_step, kern_ms=kern_ms,
+                ncopies=ncopies, ws_bytes=ws_bytes, warmup_run=warm)
 
 
 def summarize(t):
     """Throughput and both roofline fractions of one timed workload."""
     work, decode = t["work"], t["decode"]
     kern = float(t["kern_ms"].mean()) if t["kern_ms"].size else float("nan")
-    call = float(t["call_ms"].mean()) if t["call_ms"].size else float("nan")
+    call = t["ms_per_step"]
     if decode:
         per_step = work["kv_bytes"] / (t["ms_per_step"] * 1e-3) / 1e9
         ach = work["total_bytes"] / (kern * 1e-3) / 1e9
@@ -772,10 +787,10 @@ def summarize(t):
         peak, unit, bound = PEAK_BF16_TFLOPS, "TFLOP/s", "mfma"
         value_unit = "TFLOP/s"
     return dict(value=round(per_step, 3), unit=value_unit, ms_per_step=round(t["ms_per_step"], 5),
-                kernel_ms_mean=round(kern, 5), call_ms_mean=round(call, 5), bound=bound,
+                kernel_ms_mean=round(kern, 5), bound=bound,
                 achieved=round(ach, 2), achieved_call=round(ach_call, 2), peak=peak, roof_unit=unit,
                 frac=round(ach / peak, 4), frac_call=round(ach_call / peak, 4),
-                event_sampled_steps=int(t["kern_ms"].size))
+                kernel_event_steps=int(t["kern_ms"].size), warmup_steps_run=t["warmup_run"])
 
 
 def workload_config(wl, name, alibi):
@@ -818,9 +833,6 @@ def main(argv=None):
                     help="where the counter passes write (default gpurun_out/bench_counters if that "
                          "folder's parent exists, else a temporary folder)")
     ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
-    ap.add_argument("--event-every", type=int, default=4, metavar="N",
-                    help="bracket the call and its main kernel with HIP events on every N-th timed "
-                         "step (an event record costs ~3 us of stream time, so not on every step)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--counters-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV",
@@ -893,7 +905,7 @@ def main(argv=None):
         return bench_padded(args, fa, W, hip, dev, stream)
 
     props = torch.cuda.get_device_properties(dev)
-    head = time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, args.event_every,
+    head = time_workload(fa, W, hip, dev, stream, args.workload, args.steps, args.warmup, True,
                          args.dtype, args.alibi, args.seed)
     hs = summarize(head)
     wl, work = head["wl"], head["work"]
@@ -920,7 +932,7 @@ def main(argv=None):
     suite_out = {}
     if suite:
         for name in SUITE:
-            t = time_workload(fa, W, hip, dev, stream, name, args.steps, args.warmup, args.event_every,
+            t = time_workload(fa, W, hip, dev, stream, name, args.steps, args.warmup, True,
                               args.dtype, args.alibi, args.seed)
             s = summarize(t)
             s["config"] = workload_config(t["wl"], name, args.alibi)
@@ -955,8 +967,7 @@ def main(argv=None):
         "counters": counters,
         "detail": {
             "main_kernel_ms_mean": hs["kernel_ms_mean"],
-            "call_ms_mean": hs["call_ms_mean"],
-            "event_sampled_steps": hs["event_sampled_steps"],
+            "kernel_event_steps": hs["kernel_event_steps"], "warmup_steps_run": head["warmup_run"],
             "algorithmic_flop": work["flops"], "algorithmic_kv_bytes": work["kv_bytes"],
             "algorithmic_total_bytes": work["total_bytes"], "visible_pairs_per_head": work["pairs"],
             "tflops_per_step": round(work["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 3),
