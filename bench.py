@@ -28,8 +28,8 @@ for the attention kernel alone (its mean event-timed duration) and
 ``frac_call`` for the whole call (the step time: planner, attention, combine).
 
 Counters (default run; ``--no-counters`` skips them): before it touches the
-GPU, the bench runs itself three times under ``rocprofv3 --pmc`` (a short run
-of the headline workload preceded by a 1 GiB device copy):
+GPU, the bench runs itself three times under ``rocprofv3 --pmc`` (a 1 GiB
+device copy, then the usual warm-up and 3 steps of the headline workload):
   * SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, ... -> counter-derived MFMA
     utilisation of the attention kernel (busy MFMA cycles / (GPU cycles x
     SIMDs)), the shader clock it ran at, and MFMA work issued vs algorithmic;
@@ -508,6 +508,7 @@ MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES",
                  "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
                  "GRBM_GUI_ACTIVE"]
 COUNTER_PASSES = [("mfma", MFMA_COUNTERS), ("fetch", ["FETCH_SIZE"]), ("write", ["WRITE_SIZE"])]
+COUNTER_STEPS = 3  # timed steps of a counter pass (after the same warm-up as the bench)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_MIB = 1024
 XCDS = 8          # GRBM_GUI_ACTIVE is summed over the 8 XCDs
@@ -533,9 +534,12 @@ def parse_counter_csv(path):
     return vals, {k: list(v.values()) for k, v in durs.items()}
 
 
-def _mean_tail(xs):
-    """Mean over the dispatches after the first (the first one runs on a cold cache)."""
+def _mean_tail(xs, last=None):
+    """Mean over the last ``last`` dispatches (the timed steps of a counter pass,
+    after its warm-up), or over all but the first when ``last`` is None."""
     xs = list(xs)
+    if last:
+        return float(np.mean(xs[-last:]))
     return float(np.mean(xs[1:] if len(xs) > 1 else xs))
 
 
@@ -544,17 +548,18 @@ def run_counter_passes(workload, dtype, outroot, timeout_s=170):
     prof = _rocprofv3()
     if prof is None:
         return {"error": "rocprofv3 not found"}
-    res = {"workload": workload, "passes": {}, "commands": []}
+    res = {"workload": workload, "passes": {}, "commands": [], "steps": COUNTER_STEPS}
     for name, counters in COUNTER_PASSES:
         d = os.path.join(outroot, name)
         os.makedirs(d, exist_ok=True)
         cmd = ["timeout", "-s", "KILL", str(timeout_s), prof, "--pmc"] + counters + [
             "--output-format", "csv", "-d", d, "-o", "run", "--", sys.executable,
             os.path.join(ROOT, "bench.py"), "--counter-child", "--workload", workload, "--dtype", dtype,
-            "--steps", "3", "--warmup", "1"]
+            "--steps", str(COUNTER_STEPS), "--warmup", "1"]
         res["commands"].append(" ".join(["rocprofv3", "--pmc"] + counters + [
             "--output-format", "csv", "-d", os.path.relpath(d, ROOT), "-o", "run", "--", "python3", "bench.py",
-            "--counter-child", "--workload", workload, "--dtype", dtype, "--steps", "3", "--warmup", "1"]))
+            "--counter-child", "--workload", workload, "--dtype", dtype, "--steps", str(COUNTER_STEPS),
+            "--warmup", "1"]))
         print("bench: counter pass %s (%s)" % (name, " ".join(counters)), file=sys.stderr, flush=True)
         env = dict(os.environ, FA_BENCH_CHILD="1")
         import subprocess
@@ -570,7 +575,8 @@ def run_counter_passes(workload, dtype, outroot, timeout_s=170):
 
 
 def derive_counters(raw, kname, alg_flops, alg_bytes, cus):
-    """Counter-derived figures of one kernel from the three passes."""
+    """Counter-derived figures of one kernel from the three passes (averaged over
+    the pass's timed steps, one dispatch of the kernel each)."""
     if "error" in raw:
         return {"error": raw["error"]}
     out = {"kernel": None}
@@ -580,12 +586,14 @@ def derive_counters(raw, kname, alg_flops, alg_bytes, cus):
         return {"error": "%s not in the counter file" % kname}
     k = names[0]
     out["kernel"] = k
-    c = {n: _mean_tail(v) for n, v in mv[k].items()}
-    dur_ns = _mean_tail(md[k])
+    last = raw.get("steps")
+    c = {n: _mean_tail(v, last) for n, v in mv[k].items()}
+    dur_ns = _mean_tail(md[k], last)
     simds = cus * SIMDS_PER_CU
     cycles = c["GRBM_GUI_ACTIVE"] / XCDS
     out.update({
         "dispatches": len(md[k]),
+        "dispatches_averaged": min(len(md[k]), last) if last else len(md[k]) - 1,
         "profiled_kernel_us": round(dur_ns / 1e3, 2),
         "gpu_cycles": cycles,
         "sclk_ghz": round(cycles / dur_ns, 3),
@@ -613,8 +621,8 @@ def derive_counters(raw, kname, alg_flops, alg_bytes, cus):
             return float(np.mean(big))
         f_scale = copy_kib / copy_reading(fv, "FETCH_SIZE")
         w_scale = copy_kib / copy_reading(wv, "WRITE_SIZE")
-        fk = _mean_tail(fv[k]["FETCH_SIZE"])
-        wk = _mean_tail(wv[k]["WRITE_SIZE"])
+        fk = _mean_tail(fv[k]["FETCH_SIZE"], last)
+        wk = _mean_tail(wv[k]["WRITE_SIZE"], last)
         traffic = (fk * f_scale + wk * w_scale) * 1024.0
         out.update({"fetch_kib": round(fk, 1), "write_kib": round(wk, 1), "fetch_scale": round(f_scale, 4),
                     "write_scale": round(w_scale, 4), "hbm_bytes": round(traffic),
@@ -644,9 +652,9 @@ def counters_markdown(res, raw, workload, dtype, invocation):
     the bench command that ran them."""
     lines = ["# Counters of the attention kernel on workload %s (%s)" % (workload, dtype), "",
              "Each pass is a separate `rocprofv3 --pmc` run of a short bench run (1 GiB device copy,",
-             "then 1 warm-up + 3 steps); values are per dispatch, averaged over the dispatches after",
-             "the first.  MFMA utilisation = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x",
-             "1024 SIMDs).  HBM bytes = FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for",
+             "then the bench's warm-up, at least 0.2 s of steps, then %d steps); values are per" % COUNTER_STEPS,
+             "dispatch, averaged over the %d timed dispatches.  MFMA utilisation =" % COUNTER_STEPS,
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).  HBM bytes = FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for",
              "the 1 GiB copy.", "",
              "- kernel source sha256/16: `%s`" % kernel_sha()]
     for key, val in res.items():
@@ -719,7 +727,7 @@ def timed_passes(step, K, hip, events, name, reset):
 def time_workload(fa, W, hip, dev, stream, name, K, warmup, events, dtype="bf16", alibi=False, seed=None):
     """Time K calls of one workload; returns the measurements and the algorithmic work.
 
-    ``events`` False: no HIP events (counter passes)."""
+    ``events`` False: no HIP events (counter passes; their warm-up is the same)."""
     import torch
     print("bench: generating %s" % name, file=sys.stderr, flush=True)
     wl = W.make_config(name, seed, dtype=dtype)
@@ -761,7 +769,7 @@ def time_workload(fa, W, hip, dev, stream, name, K, warmup, events, dtype="bf16"
         if rc:
             raise RuntimeError(fa.fa_last_error())
 
-    warm = warm_up(step, warmup, WARMUP_MIN_S if events else 0.0)
+    warm = warm_up(step, warmup)
     ms_per_step, kern_ms = timed_passes(step, K, hip, events, name, lambda: fa.fa_varlen_set_kernel_events(0, 0))
     del copies, calls, workspace, alibi_t
     torch.cuda.empty_cache()

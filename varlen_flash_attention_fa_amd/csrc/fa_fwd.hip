@@ -713,6 +713,15 @@ attn_fwd_kernel(const FwdParams p) {
     const int kb_al = (kb / BN) * BN;
     const int seg_keys = paged ? max(BN, ((kPageCap - 1) * P / BN) * BN) : INT_MAX;
 
+    // Interior-tile copy bases without the per-tile part: this item's K/V head
+    // (and, packed, its sequence's first key row), so a tile adds one 32 x 32-bit
+    // row or page product.  Paged: the block stride in bytes.
+    const unsigned char* kh = reinterpret_cast<const unsigned char*>(
+        p.k + (paged ? (int64_t)hk * p.k_s2 : (int64_t)it.k0 * p.k_s0 + kbx + (int64_t)hk * p.k_s1));
+    const unsigned char* vh = reinterpret_cast<const unsigned char*>(
+        p.v + (paged ? (int64_t)hk * p.v_s2 : (int64_t)it.k0 * p.v_s0 + vbx + (int64_t)hk * p.v_s1));
+    const uint64_t kblkb = (uint64_t)p.k_s0 * 2u, vblkb = (uint64_t)p.v_s0 * 2u;
+
     // (an empty range, kb >= ke, runs no tile: its rows keep l = 0 and give 0)
     for (int seg0 = kb_al; kb < ke && seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
         const int seg1 = (seg_keys == INT_MAX) ? ke : min(ke, seg0 + seg_keys);
@@ -765,18 +774,20 @@ attn_fwd_kernel(const FwdParams p) {
                 constexpr int W = NI * RPI;
                 static_assert(32 % W == 0, "a wave's copy rows must stay inside one page");
                 const int wv = __builtin_amdgcn_readfirstlane(wave);  // lets the compiler keep bases scalar
+                // (block ids, slots and rows are non-negative; the fast path is only
+                // taken when a row stride fits in 24 bits)
                 const unsigned char *kw, *vw;
                 if (paged) {
                     int ws = t_slot + wv * W, wp = t_page;
                     if (ws >= P) { ws -= P; ++wp; }
                     if (ws >= P) { ws -= P; ++wp; }
-                    const int pg = __builtin_amdgcn_readfirstlane(s_pages[wp - pg_first]);
-                    kw = reinterpret_cast<const unsigned char*>(p.k + (int64_t)pg * p.k_s0 + (int64_t)ws * p.k_s1 + (int64_t)hk * p.k_s2);
-                    vw = reinterpret_cast<const unsigned char*>(p.v + (int64_t)pg * p.v_s0 + (int64_t)ws * p.v_s1 + (int64_t)hk * p.v_s2);
+                    const unsigned pg = (unsigned)__builtin_amdgcn_readfirstlane(s_pages[wp - pg_first]);
+                    kw = kh + pg * kblkb + (uint64_t)(unsigned)ws * (unsigned)p.k_rowb;
+                    vw = vh + pg * vblkb + (uint64_t)(unsigned)ws * (unsigned)p.v_rowb;
                 } else {
-                    const int64_t row = it.k0 + ts + wv * W;
-                    kw = reinterpret_cast<const unsigned char*>(p.k + row * p.k_s0 + kbx + (int64_t)hk * p.k_s1);
-                    vw = reinterpret_cast<const unsigned char*>(p.v + row * p.v_s0 + vbx + (int64_t)hk * p.v_s1);
+                    const unsigned row = (unsigned)(ts + wv * W);
+                    kw = kh + (uint64_t)row * (unsigned)p.k_rowb;
+                    vw = vh + (uint64_t)row * (unsigned)p.v_rowb;
                 }
                 const int xk = lpos ^ swk(lrow);
                 const int xv = lpos ^ swv(lrow);
