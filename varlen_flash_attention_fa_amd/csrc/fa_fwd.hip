@@ -1208,7 +1208,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int t = blockIdx.x;
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (h >= p.H) return;
-    const int nc = p.tok_nc[t];  // chunks of this token's sequence (planner), 0 if none
+    // chunks of this token's sequence (planner), 0 if none; never more than the
+    // call's bound, so no value can index past the partials
+    const int nc = min(p.tok_nc[t], p.max_chunks);
     if (nc <= 1) return;
     const float* pl = p.part_lse + (int64_t)t * p.H + h;
     const int64_t cstride_l = (int64_t)p.total_q * p.H;
