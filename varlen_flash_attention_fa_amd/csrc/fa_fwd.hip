@@ -761,9 +761,9 @@ attn_fwd_kernel(const FwdParams p) {
                     }
                 }
             }
-            const int ln = opaque_lane();
-            const int lrow = ln / CH;
-            const int lpos = ln % CH;
+            const unsigned ln = (unsigned)opaque_lane();  // unsigned: shifts, not signed division
+            const int lrow = (int)(ln / CH);
+            const int lpos = (int)(ln % CH);
             // Fast path for interior tiles: the W rows one wave copies lie in one page
             // (W divides 32, which divides P, and tiles start at multiples of BN), so
             // every copy address is a wave-uniform base (page, first row, head) plus a
@@ -791,8 +791,9 @@ attn_fwd_kernel(const FwdParams p) {
                 }
                 const int xk = lpos ^ swk(lrow);
                 const int xv = lpos ^ swv(lrow);
-                const unsigned lk_off = (unsigned)lrow * (unsigned)p.k_rowb;
-                const unsigned lv_off = (unsigned)lrow * (unsigned)p.v_rowb;
+                // (24-bit products, full rate: lrow < 64 and row strides < 2^24 here)
+                const unsigned lk_off = __umul24((unsigned)lrow, (unsigned)p.k_rowb);
+                const unsigned lv_off = __umul24((unsigned)lrow, (unsigned)p.v_rowb);
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int r0 = wv * W + i * RPI;  // tile row of the copy's first lane row (uniform)
