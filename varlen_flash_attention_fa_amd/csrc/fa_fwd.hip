@@ -1331,8 +1331,13 @@ hipError_t launch_dp(const Plan& plan, const FwdParams& p, hipStream_t s, int* s
     }
     // decode: 16 rows per wave, keys split over work items, one LDS stage: HBM
     // latency is hidden by the number of resident workgroups (LDS-limited),
-    // which beats deeper per-wave pipelines on this path
-    if (plan.wr == 1) return launch_attn<E, DP, 16, 1, 32, 1>(plan, p, s, slots);
+    // which beats deeper per-wave pipelines on this path (a second stage: paged
+    // decode -9%, MQA head dim 512 -11%), except for one-wave head dim 256 (the
+    // spec-decode batch: +1.5%, 2 workgroups of 64 KiB per CU)
+    if (plan.wr == 1) {
+        if constexpr (DP == 256) return launch_attn<E, DP, 16, 1, 32, 2>(plan, p, s, slots);
+        else return launch_attn<E, DP, 16, 1, 32, 1>(plan, p, s, slots);
+    }
     return launch_attn<E, DP, 16, 4, 32, 1>(plan, p, s, slots);
 }
 
