@@ -28,11 +28,14 @@ for the attention kernel alone (its mean event-timed duration) and
 ``frac_call`` for the whole call (the step time: planner, attention, combine).
 
 Counters (default run; ``--no-counters`` skips them): before it touches the
-GPU, the bench runs itself three times under ``rocprofv3 --pmc`` (a 1 GiB
+GPU, the bench runs itself four times under ``rocprofv3 --pmc`` (a 1 GiB
 device copy, then the usual warm-up and 3 steps of the headline workload):
   * SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE, ... -> counter-derived MFMA
     utilisation of the attention kernel (busy MFMA cycles / (GPU cycles x
     SIMDs)), the shader clock it ran at, and MFMA work issued vs algorithmic;
+  * SQ_WAVE_CYCLES, SQ_ACTIVE_INST_ANY, SQ_WAIT_INST_ANY, SQ_WAIT_ANY, ... ->
+    where each wave's cycles go (issuing, waiting for an issue slot, waiting
+    on dependencies) and the resident waves per SIMD;
   * FETCH_SIZE, then WRITE_SIZE -> the kernel's HBM bytes per launch, each
     scaled by what the same counter reads for the 1 GiB copy (``traffic``).
 
@@ -507,7 +510,12 @@ def bench_padded(args, fa, W, hip, dev, stream):
 MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY",
                  "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU",
                  "GRBM_GUI_ACTIVE"]
-COUNTER_PASSES = [("mfma", MFMA_COUNTERS), ("fetch", ["FETCH_SIZE"]), ("write", ["WRITE_SIZE"])]
+# where each wave's cycles go: issuing (ACTIVE_INST_ANY), waiting for an issue slot
+# (WAIT_INST_ANY) or waiting on dependencies, waitcnt and barriers (WAIT_ANY)
+STALL_COUNTERS = ["SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_SCA", "SQ_INSTS_SALU", "GRBM_GUI_ACTIVE"]
+COUNTER_PASSES = [("mfma", MFMA_COUNTERS), ("stall", STALL_COUNTERS), ("fetch", ["FETCH_SIZE"]),
+                  ("write", ["WRITE_SIZE"])]
 COUNTER_STEPS = 3  # timed steps of a counter pass (after the same warm-up as the bench)
 COPY_KERNEL = "__amd_rocclr_copyBuffer"
 COPY_MIB = 1024
@@ -609,6 +617,25 @@ def derive_counters(raw, kname, alg_flops, alg_bytes, cus):
         # the bf16 MFMA peak at the clock the kernel actually ran at
         "mfma_peak_at_sclk_tflops": round(cus * 4096.0 * cycles / dur_ns / 1e3, 1),
     })
+    # stall breakdown per wave (fractions of SQ_WAVE_CYCLES, same pass)
+    if "stall" in raw["passes"]:
+        sv, _ = raw["passes"]["stall"]
+        if k in sv:
+            st = {n: _mean_tail(v, last) for n, v in sv[k].items()}
+            wc = st["SQ_WAVE_CYCLES"]
+            out.update({
+                "waves_per_simd": round(wc * 4.0 / (st["GRBM_GUI_ACTIVE"] / XCDS * simds), 3),
+                "issuing_over_wave_cycles": round(st["SQ_ACTIVE_INST_ANY"] / wc, 4),
+                "issue_wait_over_wave_cycles": round(st["SQ_WAIT_INST_ANY"] / wc, 4),
+                "dependency_wait_over_wave_cycles": round(st["SQ_WAIT_ANY"] / wc, 4),
+                "valu_active_over_wave_cycles": round(st["SQ_ACTIVE_INST_VALU"] / wc, 4),
+                "lds_active_over_wave_cycles": round(st["SQ_ACTIVE_INST_LDS"] / wc, 4),
+                "scalar_active_over_wave_cycles": round(st["SQ_ACTIVE_INST_SCA"] / wc, 4),
+                "salu_insts": st["SQ_INSTS_SALU"],
+            })
+        raw_c = {"mfma:" + n: v for n, v in c.items()}
+        raw_c.update({"stall:" + n: _mean_tail(x, last) for n, x in sv.get(k, {}).items()})
+        out["raw_counters_per_dispatch"] = {n: round(v, 1) for n, v in sorted(raw_c.items())}
     # HBM traffic: FETCH_SIZE / WRITE_SIZE (KiB) scaled by the 1 GiB copy's reading
     try:
         fv, _ = raw["passes"]["fetch"]
@@ -654,7 +681,9 @@ def counters_markdown(res, raw, workload, dtype, invocation):
              "Each pass is a separate `rocprofv3 --pmc` run of a short bench run (1 GiB device copy,",
              "then the bench's warm-up, at least 0.2 s of steps, then %d steps); values are per" % COUNTER_STEPS,
              "dispatch, averaged over the %d timed dispatches.  MFMA utilisation =" % COUNTER_STEPS,
-             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).  HBM bytes = FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for",
+             "SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs).  Stall pass: each wave's",
+             "cycles (SQ_WAVE_CYCLES) split into issuing (SQ_ACTIVE_INST_ANY), waiting for an issue slot",
+             "(SQ_WAIT_INST_ANY) and waiting on dependencies, waitcnt and barriers (SQ_WAIT_ANY).  HBM bytes = FETCH_SIZE and WRITE_SIZE, each scaled by what it reads for",
              "the 1 GiB copy.", "",
              "- kernel source sha256/16: `%s`" % kernel_sha()]
     for key, val in res.items():
