@@ -238,6 +238,18 @@ def counters_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_
 
 # ----------------------------------------------------------------- CPU leg
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux /proc/cpuinfo), or an empty string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(wl, work, decode: bool, alibi=None):
     """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
     import oracle
@@ -272,7 +284,7 @@ def cpu_baseline(wl, work, decode: bool, alibi=None):
             if dt >= 10.0:
                 break
         return {"value": round(reps * kv / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-                "kind": "oracle",
+                "kind": "oracle", "cpu_model": cpu_model(),
                 "sample": "%d of %d sequences (all their query rows), %.3g GB of K/V, run %d times "
                           "in %.2f s" % (nseq, wl.batch, kv / 1e9, reps, dt)}
     # prefill: a seeded sample of query rows; metric is FLOP of those rows
@@ -289,7 +301,7 @@ def cpu_baseline(wl, work, decode: bool, alibi=None):
     oracle.attention_workload(wl, token_sel=sel, nthreads=threads, alibi_slopes=alibi)
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "%d of %d query rows (seeded), %.3g GFLOP, %.2f s" % (n, T, flops / 1e9, dt)}
 
 
@@ -307,7 +319,7 @@ def cpu_append_baseline(wl, k_new, v_new, work):
         if dt >= 10.0:
             break
     return {"value": round(reps * work["total_bytes"] / dt / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "whole append (%d tokens) run %d times in %.2f s; each oracle call also copies "
                       "both pools (it returns new ones)" % (work["total_new"], reps, dt)}
 
@@ -800,10 +812,20 @@ def time_workload(fa, W, hip, dev, stream, name, K, warmup, events, dtype="bf16"
 
     warm = warm_up(step, warmup)
     ms_per_step, kern_ms = timed_passes(step, K, hip, events, name, lambda: fa.fa_varlen_set_kernel_events(0, 0))
+    warm_ms = None
+    if events and decode and ncopies > 1:
+        # for reference only: the same K steps on one input copy, whose K/V may then
+        # be served partly from the 256 MB last-level cache
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(K):
+            step(0)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t0) * 1e3 / K
     del copies, calls, workspace, alibi_t
     torch.cuda.empty_cache()
     return dict(wl=wl, work=work, decode=decode, ms_per_step=ms_per_step, kern_ms=kern_ms,
-                ncopies=ncopies, ws_bytes=ws_bytes, warmup_run=warm)
+                ncopies=ncopies, ws_bytes=ws_bytes, warmup_run=warm, warm_ms=warm_ms)
 
 
 def summarize(t):
@@ -827,6 +849,9 @@ def summarize(t):
                 kernel_ms_mean=round(kern, 5), bound=bound,
                 achieved=round(ach, 2), achieved_call=round(ach_call, 2), peak=peak, roof_unit=unit,
                 frac=round(ach / peak, 4), frac_call=round(ach_call / peak, 4),
+                kernel_ms_p10_p50_p90=[round(float(x), 5) for x in np.percentile(t["kern_ms"], [10, 50, 90])]
+                if t["kern_ms"].size else None,
+                warm_cache_ms_per_step=round(t["warm_ms"], 5) if t.get("warm_ms") else None,
                 kernel_event_steps=int(t["kern_ms"].size), warmup_steps_run=t["warmup_run"])
 
 
@@ -1005,6 +1030,8 @@ def main(argv=None):
         "detail": {
             "main_kernel_ms_mean": hs["kernel_ms_mean"],
             "kernel_event_steps": hs["kernel_event_steps"], "warmup_steps_run": head["warmup_run"],
+            "kernel_ms_p10_p50_p90": hs["kernel_ms_p10_p50_p90"],
+            "warm_cache_ms_per_step": hs["warm_cache_ms_per_step"],
             "algorithmic_flop": work["flops"], "algorithmic_kv_bytes": work["kv_bytes"],
             "algorithmic_total_bytes": work["total_bytes"], "visible_pairs_per_head": work["pairs"],
             "tflops_per_step": round(work["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 3),
