@@ -8,7 +8,8 @@ the element-wise path), packed or paged K/V with pages of 32-256 (NaN-poisoned
 spare slots), windows unbounded, causal, sliding or two-sided, bf16 or fp16,
 and the path chosen by the planner or forced.  Forty padded (B, S, H, D) calls
 (batch-major or head-major views, Sq above or below Sk, Sk = 0 too) are compared
-the same way, and forty paged appends bit for bit against the oracle's pool.
+the same way, forty paged appends bit for bit against the oracle's pool, and
+thirty more varlen draws with ALiBi slopes (per head or per sequence).
 The draws are fixed, so every run checks the same cases; each case prints its
 parameters before it runs.
 """
@@ -17,7 +18,7 @@ import pytest
 import torch
 
 import workloads as W
-from parity_util import assert_close, run_hip
+from parity_util import assert_close, run_hip, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -165,3 +166,37 @@ def test_random_append_bit_exact(oracle_mod, i):
     gk = kp.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     gv = vp.contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
     assert int((gk != rk).sum()) == 0 and int((gv != rv).sum()) == 0, "pool differs from the oracle's"
+
+
+# ------------------------------------------------------------------ ALiBi
+
+N_ALIBI = 30
+
+
+@pytest.mark.parametrize("i", range(N_ALIBI))
+def test_random_alibi(oracle_mod, monkeypatch, i):
+    # the varlen draws above, with per-head or per-sequence slopes (seeded uniform
+    # draws in [0, 1), or the geometric sequence)
+    import varlen_flash_attention_fa_amd as fa
+    c = _draw(1000 + i)
+    rng = np.random.Generator(np.random.PCG64(9900 + i))
+    per_seq = bool(rng.random() < 0.5)
+    geometric = bool(rng.random() < 0.3)
+    slopes = W.alibi_slopes(c["H"], batch=len(c["lq"]) if per_seq else 0,
+                            seed=None if geometric else 9950 + i)
+    print("case", i, c, "per_seq", per_seq, "geometric", geometric, flush=True)
+    if c["path"]:
+        monkeypatch.setenv("FA_FORCE_PATH", c["path"])
+    else:
+        monkeypatch.delenv("FA_FORCE_PATH", raising=False)
+    wl = W.make_custom(c["lq"], c["lk"], c["H"], c["Hk"], c["D"], seed=c["seed"], page=c["page"],
+                       window_left=c["wl"], window_right=c["wr"], scale=c["scale"], poison=c["page"] > 0,
+                       dtype=c["dtype"])
+    d = to_dev(wl)
+    out, lse = fa.varlen_fwd(d["q"], d["k"], d["v"], d["cu_q"], d["cu_k"], block_table=d["bt"],
+                             page_block_size=wl.page_block_size or None, softmax_scale=wl.softmax_scale,
+                             window_left=wl.window_left, window_right=wl.window_right, return_lse=True,
+                             alibi_slopes=torch.from_numpy(slopes).cuda())
+    torch.cuda.synchronize()
+    ref_o, ref_l = oracle_mod.attention_workload(wl, alibi_slopes=slopes)
+    assert_close(out, lse, ref_o, ref_l, what="random alibi case %d" % i, n_keys=int(max([1] + c["lk"])))
