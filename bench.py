@@ -892,8 +892,7 @@ def main(argv=None):
                     help="run the counter passes for --workload too (the default run always does, "
                          "for the headline workload)")
     ap.add_argument("--counters-dir", default=None,
-                    help="where the counter passes write (default gpurun_out/bench_counters if that "
-                         "folder's parent exists, else a temporary folder)")
+                    help="where the counter passes write their files (default: a new temporary folder)")
     ap.add_argument("--counter-child", action="store_true", help=argparse.SUPPRESS)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -935,8 +934,7 @@ def main(argv=None):
         import torch  # noqa: F401
         counters_dir = args.counters_dir
         if counters_dir is None:
-            counters_dir = (os.path.join(ROOT, "gpurun_out", "bench_counters")
-                            if os.path.isdir(os.path.join(ROOT, "gpurun_out")) else tempfile.mkdtemp())
+            counters_dir = tempfile.mkdtemp(prefix="fa_bench_counters_")
         raw_counters = run_counter_passes(args.workload, args.dtype, counters_dir)
 
     import torch
