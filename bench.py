@@ -13,7 +13,9 @@ under the ``suite`` key: paged decode (64 x q_len 1, kv U[1,4096], page 32,
 H 32 / Hk 8, D 128) and the two spec-decode workloads (32 x q_len 4, kv
 U[1024,32768], page 128, D 256 MHA and D 512 MQA) as KV GB/s against HBM, and
 paged chunked prefill (16 seqs, q U[1,512] over prefixes U[0,8192], page 64)
-as TFLOP/s.  ``--workload cN`` times one workload alone.
+as TFLOP/s, and the 86-token causal batch (3 sequences of 17, 64 and 5 tokens,
+head_dim 64), whose step time is a latency figure.  ``--workload cN`` times one
+workload alone.
 
 Timed region: W untimed warm-up steps (continued, untimed, until at least 0.2 s
 of them have run, so the shader clock has settled), then exactly K steps bracketed by
@@ -866,7 +868,7 @@ def workload_config(wl, name, alibi):
 # ---------------------------------------------------------------------- main
 
 HEADLINE = "c4"
-SUITE = ["c2", "c3", "c5a", "c5b"]
+SUITE = ["c2", "c3", "c5a", "c5b", "c1"]  # c1 (86 tokens): a latency figure, its step time
 
 
 def main(argv=None):
