@@ -312,7 +312,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     __shared__ int s_wsum[kPlanThreads / 64];
     __shared__ int s_hist[kCostBuckets];
     __shared__ int s_wcnt[kPlanThreads / 64][kCostBuckets];  // per-wave bucket counts of a chunk
-    __shared__ unsigned long long s_cand[kChunkCands];
+    __shared__ unsigned s_cand[kChunkCands];
     __shared__ int s_chunk;
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -378,36 +378,36 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     const unsigned slots = (unsigned)max(1, p.slots);
     const unsigned base_units = (unsigned)carry * (unsigned)p.Hk;
     if (split && p.chunk_adapt && (base_units > slots || 4u * base_units < slots)) {
-        // item counts of every candidate chunk in one pass over the sequences
-        if (tid < kChunkCands) s_cand[tid] = 0;
+        // item counts of every candidate chunk in one pass over the sequences:
+        // lane (j, k) of a wave counts candidate k over its share of the
+        // sequences (seven per wave and round), and the partial counts meet in
+        // LDS (one add per lane, no cross-lane chains); counts stay below 2^31 /
+        // Hk, which the host checks at the smallest candidate
+        if (tid < kChunkCands) s_cand[tid] = 0u;
         __syncthreads();
-        unsigned long long cnt[kChunkCands] = {};
-        for (int b = tid; b < p.batch; b += kPlanThreads) {
-            const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-            const int tiles = ceil_div(sp.Lq * p.G, R);
-#pragma unroll
-            for (int k = 0; k < kChunkCands; ++k)
-                cnt[k] += (unsigned long long)tiles * seq_chunks(p, sp.Lk, chunk_cand(p, k));
-        }
-#pragma unroll
-        for (int k = 0; k < kChunkCands; ++k) {
-            unsigned long long x = cnt[k];
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
-            if (lane == 0 && x) atomicAdd(&s_cand[k], x);
+        constexpr int kSlots = 64 / kChunkCands;  // sequence slots per wave
+        if (lane < kSlots * kChunkCands) {
+            const int k = lane % kChunkCands;
+            const int ck = chunk_cand(p, k);
+            unsigned cnt = 0u;
+            for (int b = wave * kSlots + lane / kChunkCands; b < p.batch; b += (kPlanThreads / 64) * kSlots) {
+                const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+                cnt += (unsigned)(ceil_div(sp.Lq * p.G, R) * seq_chunks(p, sp.Lk, ck));
+            }
+            if (cnt) atomicAdd(&s_cand[k], cnt);
         }
         __syncthreads();
-        if (wave == 0) {  // one candidate per lane (unit counts < 2^31: checked on the host)
+        if (wave == 0) {  // one candidate per lane of the first 16
             unsigned long long key = ~0ull;  // (estimate, candidate) of this lane
             if (lane < kChunkCands) {
-                const unsigned units = (unsigned)s_cand[lane] * (unsigned)p.Hk;
+                const unsigned units = s_cand[lane] * (unsigned)p.Hk;
                 const unsigned long long est = (unsigned long long)((units + slots - 1) / slots) *
                                                (unsigned long long)(chunk_cand(p, lane) + 2 * R + 64);
                 key = (est << 4) | (unsigned long long)lane;
             }
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const unsigned long long y = __shfl_xor(key, o, 64);
+            for (int o = 8; o > 0; o >>= 1) {
+                const unsigned long long y = __shfl_xor(key, o, 16);
                 key = y < key ? y : key;
             }
             if (lane == 0) s_chunk = chunk_cand(p, (int)(key & 15));
@@ -444,41 +444,46 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
     // buckets, the second places each item in its bucket in item order (a stable
     // counting sort: sequence, row tile, chunk), so that the workgroups running
     // together on an XCD take neighbouring row tiles of one sequence and share
-    // its K/V window in that XCD's L2
+    // its K/V window in that XCD's L2.  When one round of threads holds every
+    // item, the second pass keeps the first one's records instead of decoding again.
+    const bool one_round = total <= kPlanThreads;
+    int bucket = -1;
+    int4 rec0 = {}, rec1 = {};
     for (int pass = 0; pass < 2; ++pass) {
         for (int base = 0; base < total; base += kPlanThreads) {
             const int i = base + tid;
-            int bucket = -1;
-            int4 rec0 = {}, rec1 = {};
-            if (i < total) {
-                int lo = 0, hi = p.batch;  // last b with off[b] <= i
-                while (hi - lo > 1) {
-                    const int mid = (lo + hi) >> 1;
-                    if (off[mid] <= i) lo = mid; else hi = mid;
+            if (pass == 0 || !one_round) {
+                bucket = -1;
+                if (i < total) {
+                    int lo = 0, hi = p.batch;  // last b with off[b] <= i
+                    while (hi - lo > 1) {
+                        const int mid = (lo + hi) >> 1;
+                        if (off[mid] <= i) lo = mid; else hi = mid;
+                    }
+                    const int b = lo;
+                    const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
+                    const int lq = sp.Lq, lk = sp.Lk;
+                    const int nc = seq_chunks(p, lk, chunk);
+                    const int local = i - off[b];
+                    const int rt = local / nc, c = local % nc;
+                    const int nrows = lq * p.G;
+                    const int r0 = rt * R, r1 = min(nrows, r0 + R) - 1;
+                    const Range a = row_range(p, r0 / p.G, lq, lk);
+                    const Range z = row_range(p, r1 / p.G, lq, lk);
+                    int kb = a.lo, ke = z.hi;
+                    if (split) {
+                        kb = max(kb, c * chunk);
+                        ke = min(ke, (c + 1) * chunk);
+                    }
+                    // every wave of the workgroup computes all its rows for every key tile,
+                    // so a partial row tile costs as much as a full one: the keys decide
+                    // (rows only break ties)
+                    const int nr = r1 - r0 + 1;
+                    const int64_t cost = (int64_t)max(0, ke - kb) * R + nr;
+                    bucket = cost_bucket(cost);
+                    rec0 = make_int4(b, rt, c | (nc << 16), chunk);
+                    rec1 = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
                 }
-                const int b = lo;
-                const SeqSpan sp = cached ? SeqSpan{s_span[b].x, s_span[b].y, s_span[b].z, s_span[b].w} : seq_span(p, b);
-                const int lq = sp.Lq, lk = sp.Lk;
-                const int nc = seq_chunks(p, lk, chunk);
-                const int local = i - off[b];
-                const int rt = local / nc, c = local % nc;
-                const int nrows = lq * p.G;
-                const int r0 = rt * R, r1 = min(nrows, r0 + R) - 1;
-                const Range a = row_range(p, r0 / p.G, lq, lk);
-                const Range z = row_range(p, r1 / p.G, lq, lk);
-                int kb = a.lo, ke = z.hi;
-                if (split) {
-                    kb = max(kb, c * chunk);
-                    ke = min(ke, (c + 1) * chunk);
-                }
-                // every wave of the workgroup computes all its rows for every key tile,
-                // so a partial row tile costs as much as a full one: the keys decide
-                // (rows only break ties)
-                const int nr = r1 - r0 + 1;
-                const int64_t cost = (int64_t)max(0, ke - kb) * R + nr;
-                bucket = cost_bucket(cost);
-                rec0 = make_int4(b, rt, c | (nc << 16), chunk);
-                rec1 = make_int4(sp.q0, sp.Lq, sp.k0, sp.Lk);
             }
             if (pass == 0) {
                 if (bucket >= 0) atomicAdd(&s_hist[bucket], 1);
@@ -497,22 +502,26 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
                 rem &= ~m;
             }
             __syncthreads();
+            // per bucket: each wave's counts become its first position (after the
+            // earlier waves and rounds), and the bucket's next free position moves on
+            if (tid < kCostBuckets) {
+                int pos = s_hist[tid];
+                for (int w = 0; w < kPlanThreads / 64; ++w) {
+                    const int n = s_wcnt[w][tid];
+                    s_wcnt[w][tid] = pos;
+                    pos += n;
+                }
+                s_hist[tid] = pos;
+            }
+            __syncthreads();
             if (bucket >= 0) {
-                int pos = s_hist[bucket] + rank;
-                for (int w = 0; w < wave; ++w) pos += s_wcnt[w][bucket];
+                const int pos = s_wcnt[wave][bucket] + rank;
                 p.items[2 * pos] = rec0;
                 p.items[2 * pos + 1] = rec1;
             }
-            __syncthreads();
-            if (tid < kCostBuckets) {  // next chunk starts after this one's items
-                int sum = 0;
-                for (int w = 0; w < kPlanThreads / 64; ++w) {
-                    sum += s_wcnt[w][tid];
-                    s_wcnt[w][tid] = 0;
-                }
-                s_hist[tid] += sum;
-            }
-            __syncthreads();
+            // this wave's row back to zero counts for the next round (only this
+            // wave reads or writes its row until the next barrier)
+            for (int k = lane; k < kCostBuckets; k += 64) s_wcnt[wave][k] = 0;
         }
         __syncthreads();
         if (pass == 0 && wave == 0) {  // bucket starts, most expensive first: one wave scan
