@@ -36,9 +36,18 @@
  *
  * Errors: every function returns FA_OK (0) or one of the FA_ERR_* codes; the
  * text of the last error on the calling thread is returned by fa_last_error().
- * On an error nothing is launched and no output is touched.  Faults inside the
- * kernels (for instance a block id outside the pool) surface at the caller's
- * next synchronization, as with any asynchronous device work.
+ * On an error nothing is launched and no output is touched.  The contents of
+ * the offset arrays and the block table are not checked by default: the
+ * kernels clamp them into the tensors they were given, so a bad table gives
+ * wrong values but no access outside the buffers.  With FA_VALIDATE=1 in the
+ * environment, fa_varlen_fwd (and fa_varlen_fwd_static) and fa_kv_append first
+ * copy those arrays to the host on `stream`, wait for the copy (the only
+ * synchronizing path of the library, meant for debugging) and return
+ * FA_ERR_ARGUMENT, launching nothing, for offsets that decrease or leave
+ * [0, rows], a sequence with more keys than its block-table row holds, or a
+ * block id outside the pool among the pages its keys (appended rows) use.
+ * Faults inside the kernels surface at the caller's next synchronization, as
+ * with any asynchronous device work.
  */
 #ifndef FA_VARLEN_H
 #define FA_VARLEN_H
@@ -125,8 +134,9 @@ int fa_varlen_workspace_bytes(const fa_tensor* q, const fa_tensor* k, const fa_t
  *       and Lk_b = cu_k[b+1] - cu_k[b] keys: non-paged, rows [cu_k[b], cu_k[b+1])
  *       of k/v; paged, logical key j lives in pool block block_table[b][j / P],
  *       slot j % P (P = page_block_size).  Rows of out past cu_q[batch] are not
- *       written.  Contents are not validated (monotone offsets, block ids inside
- *       the pool, Lk_b <= max_blocks_per_seq * P are the caller's promise).
+ *       written.  Contents are the caller's promise (monotone offsets, block ids
+ *       inside the pool, Lk_b <= max_blocks_per_seq * P), checked only with
+ *       FA_VALIDATE=1 (above).
  *   softmax_scale  multiplies q.k before the softmax.
  *   window_left, window_right  query row i of a sequence sits at key position
  *       a = i + Lk - Lq; key j is visible iff j >= a - window_left (when

@@ -18,6 +18,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <string>
+#include <vector>
 
 #include "../../include/fa_varlen.h"
 #include "fa_internal.h"
@@ -350,6 +351,107 @@ fa::Shapes padded_shapes(const fa_tensor* q, const fa_tensor* k) {
     return s;
 }
 
+// ------------------------------------------------------------ FA_VALIDATE
+//
+// The fast path trusts the contents of the offsets and the block table: the
+// kernels only clamp them into the tensors they were given (a bad table gives
+// wrong values, never an access outside the buffers).  With FA_VALIDATE=1 in
+// the environment, the forward and the append first copy those arrays to the
+// host on the call's stream, wait for them (the library's one synchronizing
+// path, for debugging) and reject what the contract forbids, launching nothing.
+
+bool validate_on() {
+    const char* e = std::getenv("FA_VALIDATE");
+    return e && std::strcmp(e, "1") == 0;
+}
+
+int copy_to_host(std::vector<int32_t>* dst, const int32_t* src, size_t n, void* stream) {
+    dst->assign(n, 0);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(dst->data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(FA_ERR_HIP, "FA_VALIDATE: copying the metadata failed: %s", hipGetErrorString(e));
+    return FA_OK;
+}
+
+// offsets: non-decreasing, within [0, limit] (limit < 0: no upper bound)
+int check_offsets(const std::vector<int32_t>& cu, const char* name, int64_t limit) {
+    for (size_t b = 0; b < cu.size(); ++b) {
+        const bool bad = cu[b] < 0 || (limit >= 0 && cu[b] > limit) || (b > 0 && cu[b] < cu[b - 1]);
+        if (bad && b == 0)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: %s must be non-decreasing within [0, %lld] (entry 0 is %d)",
+                        name, (long long)(limit >= 0 ? limit : INT32_MAX), cu[0]);
+        if (bad)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: %s must be non-decreasing within [0, %lld] (entry %zu is %d after %d)",
+                        name, (long long)(limit >= 0 ? limit : INT32_MAX), b, cu[b], cu[b - 1]);
+    }
+    return FA_OK;
+}
+
+// the block ids of keys [j0, j1) of sequence b lie in [0, num_blocks)
+int check_pages(const std::vector<int32_t>& tab, int64_t row_stride, int32_t b, int64_t j0, int64_t j1, int32_t P,
+                int64_t num_blocks) {
+    if (j1 <= j0) return FA_OK;
+    for (int64_t pg = j0 / P; pg <= (j1 - 1) / P; ++pg) {
+        const int32_t id = tab[(size_t)(b * row_stride + pg)];
+        if (id < 0 || id >= num_blocks)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: block_table[%d][%lld] = %d is outside the pool of %lld blocks",
+                        b, (long long)pg, id, (long long)num_blocks);
+    }
+    return FA_OK;
+}
+
+int copy_table(std::vector<int32_t>* dst, const fa_tensor* bt, int32_t batch, void* stream) {
+    const size_t n = batch > 0 ? (size_t)(batch - 1) * (size_t)bt->stride[0] + (size_t)bt->shape[1] : 0;
+    return copy_to_host(dst, static_cast<const int32_t*>(bt->data), n, stream);
+}
+
+// forward: offsets within q (and, packed, within k); paged, every sequence's keys
+// within the table's width and their block ids inside the pool
+int validate_fwd(const fa_tensor* q, const fa_tensor* k, const int32_t* cu_q, const int32_t* cu_k, int32_t batch,
+                 const fa_tensor* bt, int32_t P, void* stream) {
+    std::vector<int32_t> hq, hk, tab;
+    int rc = copy_to_host(&hq, cu_q, (size_t)batch + 1, stream);
+    if (!rc) rc = copy_to_host(&hk, cu_k, (size_t)batch + 1, stream);
+    if (!rc) rc = check_offsets(hq, "cu_seqlens_q", q->shape[0]);
+    if (!rc) rc = check_offsets(hk, "cu_seqlens_k", bt ? -1 : k->shape[0]);
+    if (rc || !bt) return rc;
+    rc = copy_table(&tab, bt, batch, stream);
+    const int64_t cap = bt->shape[1] * (int64_t)P;
+    for (int32_t b = 0; !rc && b < batch; ++b) {
+        const int64_t lk = (int64_t)hk[b + 1] - hk[b];
+        if (lk > cap)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: sequence %d has %lld keys, more than %lld pages of %d",
+                        b, (long long)lk, (long long)bt->shape[1], P);
+        rc = check_pages(tab, bt->stride[0], b, 0, lk, P, k->shape[0]);
+    }
+    return rc;
+}
+
+// append: new rows within k_new, each sequence's new rows at the end of its keys,
+// its keys within the table's width, the pages they land in inside the pool
+int validate_append(int64_t total_new, const int32_t* cu_new, const int32_t* cu_k, int32_t batch,
+                    const fa_tensor* bt, int32_t P, int64_t num_blocks, void* stream) {
+    std::vector<int32_t> hn, hk, tab;
+    int rc = copy_to_host(&hn, cu_new, (size_t)batch + 1, stream);
+    if (!rc) rc = copy_to_host(&hk, cu_k, (size_t)batch + 1, stream);
+    if (!rc) rc = check_offsets(hn, "cu_seqlens_new", total_new);
+    if (!rc) rc = check_offsets(hk, "cu_seqlens_k", -1);
+    if (!rc) rc = copy_table(&tab, bt, batch, stream);
+    const int64_t cap = bt->shape[1] * (int64_t)P;
+    for (int32_t b = 0; !rc && b < batch; ++b) {
+        const int64_t lk = (int64_t)hk[b + 1] - hk[b], ln = (int64_t)hn[b + 1] - hn[b];
+        if (ln > lk)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: sequence %d appends %lld rows but has %lld keys after the append",
+                        b, (long long)ln, (long long)lk);
+        if (lk > cap)
+            return fail(FA_ERR_ARGUMENT, "FA_VALIDATE: sequence %d has %lld keys, more than %lld pages of %d",
+                        b, (long long)lk, (long long)bt->shape[1], P);
+        rc = check_pages(tab, bt->stride[0], b, lk - ln, lk, P, num_blocks);
+    }
+    return rc;
+}
+
 // Device checks, plan, parameters and launch shared by both entries.  q/k/v/out
 // are rank-3 (token, head, dim) views (paged k/v: rank 4); cu arrays are only
 // read when the call is varlen.
@@ -372,9 +474,14 @@ int run_fwd(const fa_tensor* q, const fa_tensor* k, const fa_tensor* v, const fa
         return fail(FA_ERR_DEVICE, "softmax_lse must be a cuda tensor");
     if (alibi && (!alibi->data || !is_device_ptr(alibi->data)))
         return fail(FA_ERR_DEVICE, "alibi_slopes must be a cuda tensor");
+    int rc = FA_OK;
+    if (!ex.padded && validate_on()) {
+        rc = validate_fwd(q, k, cu_seqlens_q, cu_seqlens_k, batch, block_table, page_block_size, stream);
+        if (rc) return rc;
+    }
 
     fa::Plan plan;
-    int rc = fa::make_plan(ex.shapes, &plan);
+    rc = fa::make_plan(ex.shapes, &plan);
     if (rc) return fail(rc, "no launch plan for these shapes");
     if (plan.ws_bytes) {
         if (!workspace || workspace_bytes < plan.ws_bytes)
@@ -629,6 +736,11 @@ int fa_kv_append(const fa_tensor* k_new, const fa_tensor* v_new, const int32_t* 
     if (!v_new->data || !is_device_ptr(v_new->data)) return fail(FA_ERR_DEVICE, "v_new must be a cuda tensor");
     if (!k_cache->data || !is_device_ptr(k_cache->data)) return fail(FA_ERR_DEVICE, "k must be a cuda tensor");
     if (!v_cache->data || !is_device_ptr(v_cache->data)) return fail(FA_ERR_DEVICE, "v must be a cuda tensor");
+    if (validate_on()) {
+        rc = validate_append(total_new, cu_seqlens_new, cu_seqlens_k, batch, block_table, page_block_size,
+                             k_cache->shape[0], stream);
+        if (rc) return rc;
+    }
 
     fa::AppendParams p;
     std::memset(&p, 0, sizeof p);
