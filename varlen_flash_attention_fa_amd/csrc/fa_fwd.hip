@@ -1219,14 +1219,27 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
     const int h = blockIdx.y * 4 + (threadIdx.x >> 6);
     if (h >= p.H) return;
     // chunks of this token's sequence (planner), 0 if none; never more than the
-    // call's bound, so no value can index past the partials
-    const int nc = min(p.tok_nc[t], p.max_chunks);
-    if (nc <= 1) return;
+    // call's bound, so no value can index past the partials.  The first 64 chunk
+    // LSEs and the first group's partial rows are loaded beside the count (every
+    // slot below the bound is inside the partials buffer) and what lies past the
+    // count is masked after: the start is one load deep instead of three.
+    constexpr int PER = DP / 64;
+    constexpr int U = 4;  // chunks per group of loads
     const float* pl = p.part_lse + (int64_t)t * p.H + h;
     const int64_t cstride_l = (int64_t)p.total_q * p.H;
+    const float* po = p.part_o + ((int64_t)t * p.H + h) * DP + lane;
+    const int64_t cstride_o = (int64_t)p.total_q * p.H * DP;
+    const float lsp = lane < p.max_chunks ? pl[lane * cstride_l] : kNegInf;
+    float x0[U][PER];
+#pragma unroll
+    for (int q = 0; q < U; ++q)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) x0[q][e] = po[(int64_t)min(q, p.max_chunks - 1) * cstride_o + e * 64];
+    const int nc = min(p.tok_nc[t], p.max_chunks);
+    if (nc <= 1) return;
     const int64_t b = p.padded ? t / p.uniform_q : 0;  // only padded calls have per-sequence offsets
     float* lse = p.lse ? p.lse + (int64_t)h * p.lse_sh + t + b * p.lse_bx : nullptr;
-    const float l0 = lane < nc ? pl[lane * cstride_l] : kNegInf;  // the first 64 chunks
+    const float l0 = lane < nc ? lsp : kNegInf;  // the first 64 chunks
     float M = l0;
     for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, pl[c * cstride_l]);
 #pragma unroll
@@ -1238,14 +1251,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
         if (lse && lane == 0) *lse = kNegInf;
         return;
     }
-    constexpr int PER = DP / 64;
-    constexpr int U = 4;  // chunks per group of loads
     float acc[PER];
 #pragma unroll
     for (int j = 0; j < PER; ++j) acc[j] = 0.f;
     float wsum = 0.f;
-    const float* po = p.part_o + ((int64_t)t * p.H + h) * DP + lane;
-    const int64_t cstride_o = (int64_t)p.total_q * p.H * DP;
     for (int c0 = 0; c0 < nc; c0 += 64) {
         const int c = c0 + lane;
         const float lc = c0 == 0 ? l0 : (c < nc ? pl[c * cstride_l] : kNegInf);
@@ -1254,12 +1263,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const FwdParams p) {
         const int n = min(64, nc - c0);
         for (int j = 0; j < n; j += U) {
             float w[U], x[U][PER];
+            const bool first = c0 == 0 && j == 0;  // rows already loaded
 #pragma unroll
             for (int q = 0; q < U; ++q) {
                 const int jj = min(j + q, n - 1);  // a short last group repeats a chunk with weight 0
                 w[q] = j + q < n ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), jj)) : 0.f;
+                if (first) {
 #pragma unroll
-                for (int e = 0; e < PER; ++e) x[q][e] = po[(int64_t)(c0 + jj) * cstride_o + e * 64];
+                    for (int e = 0; e < PER; ++e) x[q][e] = x0[q][e];
+                } else {
+#pragma unroll
+                    for (int e = 0; e < PER; ++e) x[q][e] = po[(int64_t)(c0 + jj) * cstride_o + e * 64];
+                }
             }
 #pragma unroll
             for (int q = 0; q < U; ++q)
