@@ -545,12 +545,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const FwdParams p) {
 // Main attention kernel.
 //   DP: head dim padded to 64/128/256/512      MR: rows per wave (MFMA 32x32x16 or 16x16x32)
 //   WR: waves per workgroup (they share K/V)    BN: keys per tile     NS: LDS pipeline stages
+//   AL: the call has ALiBi slopes               DIRECT: no work list (a few sequences, no key split)
 //
 // K and V tiles live in LDS row-major ([key][d], DP*2 bytes per row) with the
 // 16-byte chunks of row r stored at position (chunk ^ swizzle(r)), so that the
 // MFMA operand reads below hit distinct banks.  Tiles start at multiples of BN;
 // rows outside [kb, ke) are loaded from the nearest valid row and masked.
-template <class E, int DP, int MR, int WR, int BN, int NS, bool AL>
+template <class E, int DP, int MR, int WR, int BN, int NS, bool AL, bool DIRECT>
 // Waves per SIMD asked of the compiler: three for the D<=128 prefill kernels,
 // with or without ALiBi (their 33 KiB of LDS allow three workgroups per CU; the
 // staggered K/V copies would otherwise raise them to 181-193 registers and two
@@ -616,7 +617,7 @@ attn_fwd_kernel(const FwdParams p) {
     // runs of 1, every XCD serves whole K/V heads.
     const unsigned wg = blockIdx.x;
     const unsigned slot = wg >> 3, chunk = (unsigned)p.xcd_chunk;
-    const unsigned unit = ((slot / chunk) * 8u + (wg & 7u)) * chunk + slot % chunk;
+    const unsigned unit = DIRECT ? wg : ((slot / chunk) * 8u + (wg & 7u)) * chunk + slot % chunk;
     const int hk = (int)(unit % (unsigned)p.Hk);
     const bool split = p.max_chunks > 1;
     const bool vec = p.vec != 0;
@@ -625,11 +626,26 @@ attn_fwd_kernel(const FwdParams p) {
     const int P = p.page;
 
     // one workgroup per work item, in the planner's order (largest first);
-    // workgroups past the end of the list exit
+    // workgroups past the end of the list exit.  Direct calls: the item is row
+    // tile rt of sequence b, spans read here, and workgroups past the sequence's
+    // row tiles exit.
     const int item_idx = (int)(unit / (unsigned)p.Hk);
-    if (item_idx >= *p.item_count) return;
     Item it;
-    {
+    if constexpr (DIRECT) {
+        const int b = item_idx / p.direct_tiles, rt = item_idx % p.direct_tiles;
+        const SeqSpan sp = seq_span(p, b);
+        if (rt >= ceil_div(sp.Lq * p.G, R)) return;
+        it.b = b;
+        it.rt = rt;
+        it.c = 0;
+        it.nc = 1;
+        it.cl = INT_MAX;
+        it.q0 = sp.q0;
+        it.Lq = sp.Lq;
+        it.k0 = sp.k0;
+        it.Lk = sp.Lk;
+    } else {
+        if (item_idx >= *p.item_count) return;
         const int4 d = p.items[2 * item_idx];
         const int4 e = p.items[2 * item_idx + 1];
         it.b = d.x;
@@ -1308,8 +1324,8 @@ hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s, int*
         int per_cu = cache.load(std::memory_order_relaxed);
         if (per_cu < 0) {
             int nb = 0;
-            const void* fn = p.alibi ? reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, true>)
-                                     : reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, false>);
+            const void* fn = p.alibi ? reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, true, false>)
+                                     : reinterpret_cast<const void*>(&attn_fwd_kernel<E, DP, MR, WR, BN, NS, false, false>);
             hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * WR, 0);
             if (e != hipSuccess) return e;
             per_cu = nb;
@@ -1328,12 +1344,19 @@ hipError_t launch_attn(const Plan& plan, const FwdParams& p, hipStream_t s, int*
         *slots = std::max(1, per_cu * cus);
         return hipSuccess;
     }
-    // one workgroup per (item, K/V head) unit, padded to whole runs on all 8 XCDs
+    // one workgroup per (item, K/V head) unit, padded to whole runs on all 8 XCDs;
+    // direct calls: one per (sequence, row tile, K/V head)
     const int64_t units = plan.items_bound * (int64_t)p.Hk;
     const int64_t run = 8 * (int64_t)p.xcd_chunk;
-    dim3 grid((unsigned)((units + run - 1) / run * run));
-    if (p.alibi) hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, true>), grid, dim3(64 * WR), 0, s, p);
-    else hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, false>), grid, dim3(64 * WR), 0, s, p);
+    if (plan.direct) {
+        const dim3 grid((unsigned)((int64_t)p.batch * plan.direct_tiles * p.Hk));
+        if (p.alibi) hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, true, true>), grid, dim3(64 * WR), 0, s, p);
+        else hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, false, true>), grid, dim3(64 * WR), 0, s, p);
+        return hipGetLastError();
+    }
+    const dim3 grid((unsigned)((units + run - 1) / run * run));
+    if (p.alibi) hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, true, false>), grid, dim3(64 * WR), 0, s, p);
+    else hipLaunchKernelGGL((attn_fwd_kernel<E, DP, MR, WR, BN, NS, false, false>), grid, dim3(64 * WR), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1455,13 +1478,14 @@ int launch_fwd(const Plan& plan, const FwdParams& p_in, void* stream, void* ev_s
     p.chunk_min = plan.chunk_min;
     p.chunk_align = plan.bn;
     p.chunk_adapt = plan.adapt ? 1 : 0;
+    p.direct_tiles = (int32_t)plan.direct_tiles;
     hipError_t e = hipSuccess;
     if (plan.adapt) {
         int slots = 0;
         e = p.f16 ? launch_main<EF16>(plan, p, s, &slots) : launch_main<EBf16>(plan, p, s, &slots);
         p.slots = slots;
     }
-    if (e == hipSuccess) {
+    if (e == hipSuccess && !plan.direct) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, p);
         e = hipGetLastError();
     }

@@ -43,6 +43,10 @@ struct FwdParams {
     int32_t* item_count;    // number of work items (per K/V head)
     int32_t* seq_off;       // [batch+1] item offsets when they do not fit in LDS
     int32_t* tok_nc;        // [total_q] chunks of each token's sequence (split only)
+    // Direct calls (a few sequences, no key split) run no planner: workgroup
+    // (b * direct_tiles + rt) * Hk + hk takes row tile rt of sequence b from the
+    // offsets itself, and exits when the sequence has fewer row tiles.
+    int32_t direct_tiles;   // row tiles of the longest possible sequence
     int32_t f16;            // element type of q/k/v/out: 0 = bf16, 1 = fp16
     const float* alibi;     // ALiBi slopes or nullptr: slope of (sequence b, head h) at alibi[b * alibi_sb + h]
     int64_t alibi_sb;
@@ -76,9 +80,14 @@ struct Plan {
     int max_chunks; // upper bound of splits per sequence
     int64_t items_bound;  // upper bound of work items per K/V head
     int xcd_chunk;        // work units per run on one XCD
+    bool direct;          // no planner: the grid covers (sequence, row tile, K/V head) directly
+    int64_t direct_tiles; // row tiles per sequence in that grid (the longest possible sequence's)
     size_t off_items, off_count, off_seq, off_tok;  // workspace layout (bytes)
     size_t ws_bytes;
 };
+
+// Largest batch that runs without the planner (when no key split is needed).
+constexpr int kDirectMaxBatch = 16;
 
 // Shapes the planner needs (host values only).
 struct Shapes {

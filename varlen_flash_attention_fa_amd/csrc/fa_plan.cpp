@@ -96,6 +96,14 @@ int make_plan(const Shapes& s, Plan* plan) {
     // runs of units per XCD: whole heads when Hk is a multiple of 8, else runs of
     // 8 units (neighbouring items of one head for Hk = 1)
     P.xcd_chunk = (s.Hk % 8 == 0) ? 1 : 8;
+    // A call with a few sequences and no key split needs no work list: its
+    // workgroups read their sequence's offsets themselves (a planner launch is
+    // about as long as the attention of such a call).  The grid is sized for any
+    // split of total_q over the sequences; workgroups past a sequence's row tiles exit.
+    // FA_DIRECT=0 keeps the planner for every call.
+    P.direct_tiles = (s.total_q * G + P.rows - 1) / P.rows;
+    P.direct = P.max_chunks == 1 && s.batch > 0 && s.batch <= kDirectMaxBatch &&
+               s.batch * P.direct_tiles * s.Hk <= 4096 && env_int("FA_DIRECT", 1) != 0;
     if ((items * s.Hk + 64) * 8 >= (int64_t)UINT32_MAX / 2) return FA_ERR_ARGUMENT;
     P.items_bound = items;
     // workspace: [split partials o][split partials lse][items][count][seq offsets]
