@@ -33,6 +33,13 @@
  * no state between calls other than the thread-local error text (and the
  * fixed scratch array of fa_varlen_fwd_static, part of its code object), and
  * never synchronizes the device: fa_varlen_fwd only enqueues kernels on `stream`.
+ * A call can therefore be captured into a HIP graph (no memset or copy nodes
+ * either); the kernels read the offsets and the block table when they run, so
+ * a replay with new contents in the same buffers computes the new lengths, as
+ * long as the tensor shapes are those of the captured call: the host sizes
+ * the grids from batch, total_q and the longest possible key range (k's rows,
+ * or the block-table width times the page size).  FA_VALIDATE=1 (below)
+ * synchronizes, so it cannot be captured.
  *
  * Errors: every function returns FA_OK (0) or one of the FA_ERR_* codes; the
  * text of the last error on the calling thread is returned by fa_last_error().
