@@ -605,6 +605,13 @@ attn_fwd_kernel(const FwdParams p) {
 
     __shared__ __attribute__((aligned(1024))) unsigned char smem[NS * 2 * TILEB];
     __shared__ int s_pages[kPageCap];
+    // Per-lane LDS read offsets of the 32-row kernels with >= 16 chunks per row,
+    // the same for every wave: the K operand base of S and the V read bases of the
+    // NPAT XOR patterns of PV.  One LDS read per tile each replaces rebuilding them
+    // from the lane id (about 13 and 16 VALU instructions per tile).
+    constexpr bool LANE_TAB = MR == 32 && CH >= 16;
+    __shared__ int s_lane_k[LANE_TAB ? 64 : 1];
+    __shared__ int4 s_lane_v[LANE_TAB ? 64 : 1];
     const unsigned smem_lds = lds_u32(smem);
 
     const int lane = threadIdx.x & 63;
@@ -746,6 +753,22 @@ attn_fwd_kernel(const FwdParams p) {
     const unsigned char* vh = reinterpret_cast<const unsigned char*>(
         p.v + (paged ? (int64_t)hk * p.v_s2 : (int64_t)it.k0 * p.v_s0 + vbx + (int64_t)hk * p.v_s1));
     const uint64_t kblkb = (uint64_t)p.k_s0 * 2u, vblkb = (uint64_t)p.v_s0 * 2u;
+
+    if constexpr (LANE_TAB) {
+        static_assert(NPAT == 4, "four V read patterns in the lane table");
+        if (threadIdx.x < 64) {
+            const int ln = threadIdx.x;
+            const int kr = kappa32(ln & 31);
+            s_lane_k[ln] = kr * ROWB + (((ln >> 5) ^ swk(kr)) << 4);
+            // V read base of rows r0 (and r0 + 4: same swizzle, one immediate 4 * ROWB on)
+            const int g16 = ln >> 4, a16 = ln & 15;
+            const int r0 = (g16 >> 1) * 8 + (a16 >> 2);
+            const int c0 = (g16 & 1) * 2 + ((a16 >> 1) & 1);
+            const int bx = r0 * ROWB + ((c0 ^ swv(r0)) << 4) + (a16 & 1) * 8;
+            s_lane_v[ln] = int4{bx, bx ^ (CPD << 4), bx ^ ((2 * CPD) << 4), bx ^ ((3 * CPD) << 4)};
+        }
+        __syncthreads();
+    }
 
     // (an empty range, kb >= ke, runs no tile: its rows keep l = 0 and give 0)
     for (int seg0 = kb_al; kb < ke && seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
@@ -912,6 +935,8 @@ attn_fwd_kernel(const FwdParams p) {
         }
 
         for (int t = 0; t < ntiles; ++t) {
+            int kb_lane = 0;  // this lane's K operand base (lane table), read before the waits
+            if constexpr (LANE_TAB) kb_lane = s_lane_k[lane];
             if constexpr (NS == 1) {
                 wait_vmcnt<0>();  // K(t) has landed (no other copy is in flight)
                 __syncthreads();  // K(t) visible to every wave; every wave is done with V(t-1)
@@ -938,9 +963,14 @@ attn_fwd_kernel(const FwdParams p) {
             constexpr int SPU = MR / 2;  // score values per lane per 32-key unit
             float sc[NU][SPU];
             if constexpr (MR == 32) {
-                const int ln = opaque_lane();
-                const int kr = kappa32(ln & 31);
-                const int kbase = kr * ROWB + (((ln >> 5) ^ swk(kr)) << 4);
+                int kbase;
+                if constexpr (LANE_TAB) {
+                    kbase = kb_lane;
+                } else {
+                    const int ln = opaque_lane();
+                    const int kr = kappa32(ln & 31);
+                    kbase = kr * ROWB + (((ln >> 5) ^ swk(kr)) << 4);
+                }
                 auto kread = [&](int u, int st) {
                     return *reinterpret_cast<const u32x4*>(kbuf + (kbase ^ (st << 5)) + u * 32 * ROWB);
                 };
@@ -1114,6 +1144,8 @@ attn_fwd_kernel(const FwdParams p) {
             }
             l_run += rs;
 
+            int4 vx_lane = {};  // V read bases (lane table), read before the wait
+            if constexpr (LANE_TAB) vx_lane = s_lane_v[lane];
             if constexpr (NS == 1) {
                 // V(t) has landed: only K(t+1)'s NI copies per lane may still be in flight
                 if (t + 1 < ntiles) wait_vmcnt<NI>();
@@ -1127,17 +1159,26 @@ attn_fwd_kernel(const FwdParams p) {
             // groups add whole rows (the swizzle depends on the row mod 16 only) and
             // d-blocks past the swizzled bits add a whole chunk group, both constants.
             {
-                const int ln = opaque_lane();
-                const int g16 = ln >> 4, a16 = ln & 15;
-                const int r0 = (MR == 32) ? (g16 >> 1) * 8 + (a16 >> 2) : g16 * 8 + (a16 >> 2);
-                const int c0 = (MR == 32) ? (g16 & 1) * 2 + ((a16 >> 1) & 1) : (a16 >> 1) & 1;
                 int vx[NPAT][2];
+                if constexpr (LANE_TAB) {
+                    const int vv[4] = {vx_lane.x, vx_lane.y, vx_lane.z, vx_lane.w};
 #pragma unroll
-                for (int h2 = 0; h2 < 2; ++h2) {
-                    const int rr = r0 + 4 * h2;
-                    const int bx = rr * ROWB + ((c0 ^ swv(rr)) << 4) + (a16 & 1) * 8;
+                    for (int pat = 0; pat < NPAT; ++pat) {
+                        vx[pat][0] = vv[pat];
+                        vx[pat][1] = vv[pat] + 4 * ROWB;
+                    }
+                } else {
+                    const int ln = opaque_lane();
+                    const int g16 = ln >> 4, a16 = ln & 15;
+                    const int r0 = (MR == 32) ? (g16 >> 1) * 8 + (a16 >> 2) : g16 * 8 + (a16 >> 2);
+                    const int c0 = (MR == 32) ? (g16 & 1) * 2 + ((a16 >> 1) & 1) : (a16 >> 1) & 1;
 #pragma unroll
-                    for (int pat = 0; pat < NPAT; ++pat) vx[pat][h2] = bx ^ ((pat * CPD) << 4);
+                    for (int h2 = 0; h2 < 2; ++h2) {
+                        const int rr = r0 + 4 * h2;
+                        const int bx = rr * ROWB + ((c0 ^ swv(rr)) << 4) + (a16 & 1) * 8;
+#pragma unroll
+                        for (int pat = 0; pat < NPAT; ++pat) vx[pat][h2] = bx ^ ((pat * CPD) << 4);
+                    }
                 }
                 if constexpr (MR == 32) {
                     // MFMA i: unit i / (2 NDB), 16-key half (i / NDB) % 2, d-block i % NDB;
