@@ -612,6 +612,11 @@ attn_fwd_kernel(const FwdParams p) {
     constexpr bool LANE_TAB = MR == 32 && CH >= 16;
     __shared__ int s_lane_k[LANE_TAB ? 64 : 1];
     __shared__ int4 s_lane_v[LANE_TAB ? 64 : 1];
+    // and each thread's per-lane offsets of its NI = 4 interior-tile K copies
+    // ([0, NT)) and V copies ([NT, 2 NT)), read once per tile instead of rebuilt
+    // (not with ALiBi: there the table's values spill inside the tile loop)
+    constexpr bool CP_TAB = LANE_TAB && !AL;
+    __shared__ int4 s_cp_off[CP_TAB ? 2 * NT : 1];
     const unsigned smem_lds = lds_u32(smem);
 
     const int lane = threadIdx.x & 63;
@@ -767,8 +772,28 @@ attn_fwd_kernel(const FwdParams p) {
             const int bx = r0 * ROWB + ((c0 ^ swv(r0)) << 4) + (a16 & 1) * 8;
             s_lane_v[ln] = int4{bx, bx ^ (CPD << 4), bx ^ ((2 * CPD) << 4), bx ^ ((3 * CPD) << 4)};
         }
+        if constexpr (CP_TAB) {
+            // the interior-tile copy offsets of issue() below (only used when its
+            // fast path is taken: row strides below 2^24)
+            static_assert(NI == 4, "four copies per tensor in the copy-offset table");
+            constexpr int W = NI * RPI;
+            const int lrow = lane / CH, lpos = lane % CH;
+            const int xk = lpos ^ swk(lrow), xv = lpos ^ swv(lrow);
+            const unsigned lk_off = __umul24((unsigned)lrow, (unsigned)p.k_rowb);
+            const unsigned lv_off = __umul24((unsigned)lrow, (unsigned)p.v_rowb);
+            int ko[NI], vo[NI];
+#pragma unroll
+            for (int i = 0; i < NI; ++i) {
+                const int r0 = wave * W + i * RPI;
+                ko[i] = (int)(lk_off + ((unsigned)(xk ^ swk(r0)) << 4));
+                vo[i] = (int)(lv_off + ((unsigned)(xv ^ swv(r0)) << 4));
+            }
+            s_cp_off[threadIdx.x] = int4{ko[0], ko[1], ko[2], ko[3]};
+            s_cp_off[NT + threadIdx.x] = int4{vo[0], vo[1], vo[2], vo[3]};
+        }
         __syncthreads();
     }
+    int4 cp_k = {}, cp_v = {};  // this thread's copy offsets (table), loaded ahead of issue()
 
     // (an empty range, kb >= ke, runs no tile: its rows keep l = 0 and give 0)
     for (int seg0 = kb_al; kb < ke && seg0 < ke; seg0 = (seg_keys == INT_MAX ? ke : seg0 + seg_keys)) {
@@ -842,11 +867,19 @@ attn_fwd_kernel(const FwdParams p) {
                 // (24-bit products, full rate: lrow < 64 and row strides < 2^24 here)
                 const unsigned lk_off = __umul24((unsigned)lrow, (unsigned)p.k_rowb);
                 const unsigned lv_off = __umul24((unsigned)lrow, (unsigned)p.v_rowb);
+                const int tk[4] = {cp_k.x, cp_k.y, cp_k.z, cp_k.w};
+                const int tv[4] = {cp_v.x, cp_v.y, cp_v.z, cp_v.w};
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
                     const int r0 = wv * W + i * RPI;  // tile row of the copy's first lane row (uniform)
-                    const unsigned vk = lk_off + ((unsigned)(xk ^ swk(r0)) << 4);
-                    const unsigned vv = lv_off + ((unsigned)(xv ^ swv(r0)) << 4);
+                    unsigned vk, vv;
+                    if constexpr (CP_TAB) {
+                        vk = (unsigned)tk[i];
+                        vv = (unsigned)tv[i];
+                    } else {
+                        vk = lk_off + ((unsigned)(xk ^ swk(r0)) << 4);
+                        vv = lv_off + ((unsigned)(xv ^ swv(r0)) << 4);
+                    }
                     const unsigned dst = smem_lds + (unsigned)((t % NS) * 2 * TILEB + (wv * NI + i) * 1024);
                     if (which != 1) copy16_to_lds_sv(kw + (size_t)(i * RPI) * p.k_rowb, vk, dst);
                     if (which != 0) copy16_to_lds_sv(vw + (size_t)(i * RPI) * p.v_rowb, vv, dst + TILEB);
@@ -923,6 +956,10 @@ attn_fwd_kernel(const FwdParams p) {
         // of tile t run, K(t+1) while the softmax and PV of tile t run; each
         // buffer is refilled once every wave is past its last read of it.
         // NS >= 2: whole tiles NS-1 ahead.
+        if constexpr (CP_TAB) {
+            cp_k = s_cp_off[threadIdx.x];
+            cp_v = s_cp_off[NT + threadIdx.x];
+        }
         if constexpr (NS == 1) {
             if (ntiles > 0) {
                 __syncthreads();  // every wave is done with the previous segment's K tile
@@ -937,6 +974,10 @@ attn_fwd_kernel(const FwdParams p) {
         for (int t = 0; t < ntiles; ++t) {
             int kb_lane = 0;  // this lane's K operand base (lane table), read before the waits
             if constexpr (LANE_TAB) kb_lane = s_lane_k[lane];
+            if constexpr (CP_TAB) {
+                cp_v = s_cp_off[NT + threadIdx.x];
+                if constexpr (NS > 1) cp_k = s_cp_off[threadIdx.x];
+            }
             if constexpr (NS == 1) {
                 wait_vmcnt<0>();  // K(t) has landed (no other copy is in flight)
                 __syncthreads();  // K(t) visible to every wave; every wave is done with V(t-1)
@@ -1063,6 +1104,7 @@ attn_fwd_kernel(const FwdParams p) {
             }
 
             if constexpr (NS == 1) {
+                if constexpr (CP_TAB) cp_k = s_cp_off[threadIdx.x];
                 __syncthreads();  // every wave is done with K(t)
                 if (t + 1 < ntiles) issue(t + 1, 0);
             }
