@@ -773,8 +773,10 @@ attn_fwd_kernel(const FwdParams p) {
             s_lane_v[ln] = int4{bx, bx ^ (CPD << 4), bx ^ ((2 * CPD) << 4), bx ^ ((3 * CPD) << 4)};
         }
         if constexpr (CP_TAB) {
-            // the interior-tile copy offsets of issue() below (only used when its
-            // fast path is taken: row strides below 2^24)
+            // the interior-tile copy offsets of issue() below, each copy's first row
+            // included so that the four copies share one scalar base (only used when
+            // its fast path is taken: row strides below 2^24, so every offset stays
+            // below 2^28)
             static_assert(NI == 4, "four copies per tensor in the copy-offset table");
             constexpr int W = NI * RPI;
             const int lrow = lane / CH, lpos = lane % CH;
@@ -785,8 +787,8 @@ attn_fwd_kernel(const FwdParams p) {
 #pragma unroll
             for (int i = 0; i < NI; ++i) {
                 const int r0 = wave * W + i * RPI;
-                ko[i] = (int)(lk_off + ((unsigned)(xk ^ swk(r0)) << 4));
-                vo[i] = (int)(lv_off + ((unsigned)(xv ^ swv(r0)) << 4));
+                ko[i] = (int)(lk_off + (unsigned)(i * RPI) * (unsigned)p.k_rowb + ((unsigned)(xk ^ swk(r0)) << 4));
+                vo[i] = (int)(lv_off + (unsigned)(i * RPI) * (unsigned)p.v_rowb + ((unsigned)(xv ^ swv(r0)) << 4));
             }
             s_cp_off[threadIdx.x] = int4{ko[0], ko[1], ko[2], ko[3]};
             s_cp_off[NT + threadIdx.x] = int4{vo[0], vo[1], vo[2], vo[3]};
@@ -881,8 +883,11 @@ attn_fwd_kernel(const FwdParams p) {
                         vv = lv_off + ((unsigned)(xv ^ swv(r0)) << 4);
                     }
                     const unsigned dst = smem_lds + (unsigned)((t % NS) * 2 * TILEB + (wv * NI + i) * 1024);
-                    if (which != 1) copy16_to_lds_sv(kw + (size_t)(i * RPI) * p.k_rowb, vk, dst);
-                    if (which != 0) copy16_to_lds_sv(vw + (size_t)(i * RPI) * p.v_rowb, vv, dst + TILEB);
+                    // (table offsets hold the copy's first row; otherwise the base does)
+                    const size_t krow = CP_TAB ? 0 : (size_t)(i * RPI) * p.k_rowb;
+                    const size_t vrow = CP_TAB ? 0 : (size_t)(i * RPI) * p.v_rowb;
+                    if (which != 1) copy16_to_lds_sv(kw + krow, vk, dst);
+                    if (which != 0) copy16_to_lds_sv(vw + vrow, vv, dst + TILEB);
                 }
                 return;
             }
