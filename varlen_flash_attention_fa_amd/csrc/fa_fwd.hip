@@ -817,6 +817,10 @@ attn_fwd_kernel(const FwdParams p) {
         int nx_page[2] = {pg_first, pg_first}, nx_slot[2] = {0, 0};
         const int pg_last = paged ? (seg1 - 1) / P : 0;
         if (paged) nx_slot[0] = nx_slot[1] = seg0 - pg_first * P;
+        // block id and slot of this wave's rows in the last K tile issued on the
+        // fast path: V of the same tile, issued next, reuses them
+        unsigned pg_c = 0;
+        int ws_c = 0;
 
         // issue the copies of tile t of this segment into stage t % NS: which = 0
         // K only, 1 V only, 2 both
@@ -853,10 +857,21 @@ attn_fwd_kernel(const FwdParams p) {
                 // taken when a row stride fits in 24 bits)
                 const unsigned char *kw, *vw;
                 if (paged) {
-                    int ws = t_slot + wv * W, wp = t_page;
-                    if (ws >= P) { ws -= P; ++wp; }
-                    if (ws >= P) { ws -= P; ++wp; }
-                    const unsigned pg = (unsigned)__builtin_amdgcn_readfirstlane(s_pages[wp - pg_first]);
+                    unsigned pg;
+                    int ws;
+                    if (which == 1) {
+                        // V(t) alone follows K(t), which took this path too (same tile)
+                        pg = pg_c;
+                        ws = ws_c;
+                    } else {
+                        int wp = t_page;
+                        ws = t_slot + wv * W;
+                        if (ws >= P) { ws -= P; ++wp; }
+                        if (ws >= P) { ws -= P; ++wp; }
+                        pg = (unsigned)__builtin_amdgcn_readfirstlane(s_pages[wp - pg_first]);
+                        pg_c = pg;
+                        ws_c = ws;
+                    }
                     kw = kh + pg * kblkb + (uint64_t)(unsigned)ws * (unsigned)p.k_rowb;
                     vw = vh + pg * vblkb + (uint64_t)(unsigned)ws * (unsigned)p.v_rowb;
                 } else {
