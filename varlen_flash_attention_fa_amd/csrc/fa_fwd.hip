@@ -562,7 +562,7 @@ template <class E, int DP, int MR, int WR, int BN, int NS, bool AL, bool DIRECT>
 // its 64 KiB of LDS allow two workgroups per CU).
 __global__ __launch_bounds__(64 * WR) __attribute__((amdgpu_waves_per_eu(
     (WR == 4 && DP <= 128 && MR == 32) ? 3
-    : ((WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256) || (WR == 1 && DP <= 256)) ? 2
+    : ((WR == 4 && DP <= 128) || (WR == 4 && MR == 16 && NS == 1 && DP >= 256) || (WR == 1 && DP <= 128)) ? 2
     : 1, 8))) void
 attn_fwd_kernel(const FwdParams p) {
     typedef Mfma<MR, E> M;
