@@ -1284,35 +1284,42 @@ attn_fwd_kernel(const FwdParams p) {
         }
     }
 
-    // ---- epilogue
+    // ---- epilogue.  The lane's row, head and column group are rebuilt from the
+    // lane id: kept from the prologue, they (and 64-bit products of them) lived
+    // across the tile loop and spilled.
     const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
     const float lse2 = l_run > 0.f ? m_run + __builtin_amdgcn_logf(l_run) : kNegInf;
-    const int tq = it.q0 + qi;
+    const int lane_e = opaque_lane();
+    const int kgrp_e = lane_e / MR;
+    const int r_e = r_first + wave * MR + lane_e % MR;
+    const bool row_ok_e = r_e < nrows;
+    const int tq = it.q0 + (row_ok_e ? r_e / p.G : 0);
+    const int h_e = hk * p.G + (row_ok_e ? r_e % p.G : 0);
     if (split && it.nc > 1) {
-        if (row_ok) {
-            float* po = p.part_o + (((int64_t)it.c * p.total_q + tq) * p.H + h) * DP;
+        if (row_ok_e) {
+            float* po = p.part_o + (((int64_t)it.c * p.total_q + tq) * p.H + h_e) * DP;
 #pragma unroll
             for (int db = 0; db < NDB; ++db)
 #pragma unroll
                 for (int v4 = 0; v4 < M::NACC; v4 += 4) {
                     int d;
-                    if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
-                    else d = db * 16 + kgrp * 4;
+                    if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp_e * 4;
+                    else d = db * 16 + kgrp_e * 4;
                     f32x4 val = {o[db][v4] * inv, o[db][v4 + 1] * inv, o[db][v4 + 2] * inv,
                                  o[db][v4 + 3] * inv};
                     *reinterpret_cast<f32x4*>(po + d) = val;
                 }
-            if (kgrp == 0) p.part_lse[((int64_t)it.c * p.total_q + tq) * p.H + h] = lse2;
+            if (kgrp_e == 0) p.part_lse[((int64_t)it.c * p.total_q + tq) * p.H + h_e] = lse2;
         }
-    } else if (row_ok) {
-        uint16_t* orow = p.out + (int64_t)tq * p.o_s0 + (int64_t)it.b * p.o_bx + (int64_t)h * p.o_s1;
+    } else if (row_ok_e) {
+        uint16_t* orow = p.out + (int64_t)tq * p.o_s0 + (int64_t)it.b * p.o_bx + (int64_t)h_e * p.o_s1;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
 #pragma unroll
             for (int v4 = 0; v4 < M::NACC; v4 += 4) {
                 int d;
-                if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp * 4;
-                else d = db * 16 + kgrp * 4;
+                if constexpr (MR == 32) d = db * 32 + (v4 >> 2) * 8 + kgrp_e * 4;
+                else d = db * 16 + kgrp_e * 4;
                 if (d >= D) continue;
                 const float x0 = o[db][v4] * inv, x1 = o[db][v4 + 1] * inv;
                 const float x2 = o[db][v4 + 2] * inv, x3 = o[db][v4 + 3] * inv;
@@ -1325,7 +1332,7 @@ attn_fwd_kernel(const FwdParams p) {
                         if (d + j < D) orow[d + j] = E::one(xs[j]);
                 }
             }
-        if (p.lse && kgrp == 0) p.lse[(int64_t)h * p.lse_sh + tq + (int64_t)it.b * p.lse_bx] = lse2 * 0.6931471805599453f;
+        if (p.lse && kgrp_e == 0) p.lse[(int64_t)h_e * p.lse_sh + tq + (int64_t)it.b * p.lse_bx] = lse2 * 0.6931471805599453f;
     }
 }
 
