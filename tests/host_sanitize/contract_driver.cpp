@@ -4,11 +4,13 @@
 // or returns before any device work).  Each case states the status it must
 // return; a mismatch, or any sanitizer report, fails the test.
 #include <climits>
+#include <cstdlib>
 #include <cstdio>
 #include <cstring>
 #include <vector>
 
 #include "../../include/fa_varlen.h"
+#include "../../varlen_flash_attention_fa_amd/csrc/fa_internal.h"
 
 namespace {
 
@@ -168,6 +170,43 @@ int main() {
     std::vector<int32_t> cun = {0, 2, 4, 6};
     expect("append host", fa_kv_append(&KN, &KN, cun.data(), cu.data(), 3, &BT3, &KC, &KC, 32, nullptr),
            FA_ERR_DEVICE);
+
+    // direct calls (no planner): a few sequences, no key split, a bounded grid;
+    // the grid's row tiles cover every split of total_q over the sequences
+    struct DC { long long tq, H, Hk, D, max_lk, batch; bool paged; bool direct; long long tiles; const char* what; } dc[] = {
+        {86, 4, 2, 64, 86, 3, false, true, 3, "c1: 3 sequences, decode path"},
+        {64, 32, 8, 128, 4096, 64, true, false, 0, "c2: 64 sequences"},
+        {4104, 32, 8, 128, 8704, 16, true, false, 0, "c3: 16 sequences, grid over 4096 units"},
+        {1024, 8, 2, 128, 1500, 16, false, true, 32, "16 sequences, 1024 rows"},
+        {1024, 8, 2, 128, 1500, 17, false, false, 0, "17 sequences"},
+        {4, 32, 8, 128, 5000, 4, true, false, 0, "decode with a key split"},
+        {4, 32, 8, 128, 512, 4, true, true, 1, "decode, one chunk"},
+    };
+    for (const auto& c : dc) {
+        fa::Shapes sh;
+        sh.total_q = c.tq; sh.H = c.H; sh.Hk = c.Hk; sh.D = c.D; sh.max_lk = c.max_lk; sh.batch = c.batch;
+        sh.paged = c.paged;
+        fa::Plan pl;
+        expect(c.what, fa::make_plan(sh, &pl), FA_OK);
+        if (pl.direct != c.direct || (c.direct && pl.direct_tiles != c.tiles) ||
+            (pl.direct && pl.direct_tiles * pl.rows < c.tq * (c.H / c.Hk))) {
+            std::printf("MISMATCH %s: direct %d tiles %lld (rows %d)\n", c.what, (int)pl.direct,
+                        (long long)pl.direct_tiles, pl.rows);
+            ++g_bad;
+        }
+    }
+    {
+        setenv("FA_DIRECT", "0", 1);  // keeps the planner for every call
+        fa::Shapes sh;
+        sh.total_q = 86; sh.H = 4; sh.Hk = 2; sh.D = 64; sh.max_lk = 86; sh.batch = 3; sh.paged = false;
+        fa::Plan pl;
+        expect("FA_DIRECT=0", fa::make_plan(sh, &pl), FA_OK);
+        if (pl.direct) {
+            std::printf("MISMATCH FA_DIRECT=0: direct\n");
+            ++g_bad;
+        }
+        unsetenv("FA_DIRECT");
+    }
 
     std::printf("contract driver: %d mismatches\n", g_bad);
     return g_bad ? 1 : 0;
