@@ -697,7 +697,9 @@ attn_fwd_kernel(const FwdParams p) {
     const int qi = row_ok ? r / p.G : 0;
     const int g = row_ok ? r % p.G : 0;
     const int h = hk * p.G + g;
-    int lo = INT_MIN, hi = INT_MAX;
+    // (rows past the item keep the item's range: in-range bounds, whatever they
+    // compute is never stored)
+    int lo = kb, hi = ke;
     if (row_ok) {
         const Range rr = row_range(p, qi, Lq, Lk);
         lo = max(rr.lo, kb);
@@ -1152,15 +1154,19 @@ attn_fwd_kernel(const FwdParams p) {
             const bool need_mask = !(w_lo <= n0 && w_hi >= n0 + BN);
             float mx = kNegInf;
             if (need_mask) {
+                // key n0 + 8 kgrp + c of score e against [lo, hi): the bounds are taken
+                // relative to the lane's first key once, so each score compares its
+                // compile-time c (lo and hi lie in [kb, ke], so nothing overflows)
+                const int kl = n0 + kgrp * 8;
+                const int dlo = lo - kl, dhi = hi - kl;
 #pragma unroll
                 for (int u = 0; u < NU; ++u)
 #pragma unroll
                     for (int e = 0; e < SPU; ++e) {
-                        int key;
-                        if constexpr (MR == 32) key = u * 32 + (e >> 3) * 16 + kgrp * 8 + (e & 7);
-                        else key = u * 32 + kgrp * 8 + e;
-                        const int n = n0 + key;
-                        if (n < lo || n >= hi) sc[u][e] = kNegInf;
+                        int c;
+                        if constexpr (MR == 32) c = u * 32 + (e >> 3) * 16 + (e & 7);
+                        else c = u * 32 + e;
+                        if (c < dlo || c >= dhi) sc[u][e] = kNegInf;
                     }
             }
 #pragma unroll
