@@ -28,6 +28,8 @@ dependent kernels holds the stream for about 5 us, which is why the step time
 is taken without them.  Each entry reports two roofline fractions: ``frac``
 for the attention kernel alone (its mean event-timed duration) and
 ``frac_call`` for the whole call (the step time: planner, attention, combine).
+The 86-token batch is also timed from a HIP graph of 32 captured calls replayed
+10 times (``graph_replay_ms_per_step``): its latency without per-call host work.
 
 Counters (default run; ``--no-counters`` skips them): before it touches the
 GPU, the bench runs itself four times under ``rocprofv3 --pmc`` (a 1 GiB
@@ -824,10 +826,31 @@ def time_workload(fa, W, hip, dev, stream, name, K, warmup, events, dtype="bf16"
             step(0)
         torch.cuda.synchronize()
         warm_ms = (time.perf_counter() - t0) * 1e3 / K
+    graph_ms = None
+    if events and name == "c1":
+        # the latency workload once more without per-call host work: 32 calls
+        # captured in one HIP graph (a call enqueues kernels only), the graph
+        # replayed 10 times; one graph launch costs tens of microseconds of host
+        # time, which 32 calls amortise
+        G, R = 32, 10
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for i in range(G):
+                step(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(R):
+            g.replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - t0) * 1e3 / (R * G)
+        del g
     del copies, calls, workspace, alibi_t
     torch.cuda.empty_cache()
     return dict(wl=wl, work=work, decode=decode, ms_per_step=ms_per_step, kern_ms=kern_ms,
-                ncopies=ncopies, ws_bytes=ws_bytes, warmup_run=warm, warm_ms=warm_ms)
+                ncopies=ncopies, ws_bytes=ws_bytes, warmup_run=warm, warm_ms=warm_ms, graph_ms=graph_ms)
 
 
 def summarize(t):
@@ -854,6 +877,7 @@ def summarize(t):
                 kernel_ms_p10_p50_p90=[round(float(x), 5) for x in np.percentile(t["kern_ms"], [10, 50, 90])]
                 if t["kern_ms"].size else None,
                 warm_cache_ms_per_step=round(t["warm_ms"], 5) if t.get("warm_ms") else None,
+                graph_replay_ms_per_step=round(t["graph_ms"], 5) if t.get("graph_ms") else None,
                 kernel_event_steps=int(t["kern_ms"].size), warmup_steps_run=t["warmup_run"])
 
 
@@ -1032,6 +1056,7 @@ def main(argv=None):
             "kernel_event_steps": hs["kernel_event_steps"], "warmup_steps_run": head["warmup_run"],
             "kernel_ms_p10_p50_p90": hs["kernel_ms_p10_p50_p90"],
             "warm_cache_ms_per_step": hs["warm_cache_ms_per_step"],
+            "graph_replay_ms_per_step": hs["graph_replay_ms_per_step"],
             "algorithmic_flop": work["flops"], "algorithmic_kv_bytes": work["kv_bytes"],
             "algorithmic_total_bytes": work["total_bytes"], "visible_pairs_per_head": work["pairs"],
             "tflops_per_step": round(work["flops"] / (head["ms_per_step"] * 1e-3) / 1e12, 3),
