@@ -10,8 +10,9 @@ and the path chosen by the planner or forced.  Forty padded (B, S, H, D) calls
 (batch-major or head-major views, Sq above or below Sk, Sk = 0 too) are compared
 the same way, forty paged appends bit for bit against the oracle's pool, and
 thirty more varlen draws with ALiBi slopes (per head or per sequence).
-The draws are fixed, so every run checks the same cases; each case prints its
-parameters before it runs.
+Every fourth varlen case runs a second time through the planner's work list
+(FA_DIRECT=0) and must give the same bits.  The draws are fixed, so every run
+checks the same cases; each case prints its parameters before it runs.
 """
 import numpy as np
 import pytest
@@ -73,6 +74,14 @@ def test_random_shape(oracle_mod, monkeypatch, i):
     out, lse = run_hip(wl)
     ref_o, ref_l = oracle_mod.attention_workload(wl)
     assert_close(out, lse, ref_o, ref_l, what="random case %d" % i, n_keys=int(max([1] + c["lk"])))
+    if i % 4 == 0:
+        # the same call through the planner's work list (these small batches
+        # otherwise run as direct calls when their keys are not split): same bits
+        monkeypatch.setenv("FA_DIRECT", "0")
+        out2, lse2 = run_hip(wl)
+        monkeypatch.delenv("FA_DIRECT")
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "random case %d: planned" % i
+        assert torch.equal(lse, lse2), "random case %d: planned lse" % i
 
 
 # ------------------------------------------------------------ padded entry
